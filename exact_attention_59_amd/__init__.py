@@ -1,0 +1,196 @@
+"""exact_attention_59_amd -- exact attention on MI355X through the C ABI of libfa.so.
+
+A thin ctypes binding: every function below validates torch tensors, passes their
+device pointers and the current HIP stream to the function of the same name in
+``include/fa.h``, and raises on a non-zero status.  All arithmetic runs in the
+gfx950 kernels; there is no CPU fallback.  PyTorch is used only to hold device
+memory and to name the stream.
+
+    fwd(q, k, v, causal=False, scale=None)   -> (o, lse)          fa_fwd
+    decode_split(q, k, v, num_splits, scale) -> (o_part, lse_part) fa_decode_split
+    combine(o_part, lse_part)                -> (o, lse)          fa_combine
+    decode(q, k, v, num_splits=None, scale)  -> (o, lse)          both, on one stream
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "decode_split", "combine", "decode", "decode_num_splits", "decode_workspace_bytes",
+           "fwd_tile_shape", "fwd_tile_count", "strerror", "library", "library_path", "FAError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libfa.so")
+_lib = None
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = range(7)
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, strerror(status)))
+        self.status = status
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def library():
+    """Load libfa.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError("libfa.so is not built (%s); run `python -m exact_attention_59_amd.build` "
+                              "or __graft_entry__.build()" % LIBRARY)
+        lib = ctypes.CDLL(LIBRARY)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_decode_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
+        lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_tile_shape.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.fa_fwd_tile_count.argtypes = [i32, i32, i32, i32]
+        lib.fa_fwd_tile_count.restype = ctypes.c_longlong
+        lib.fa_strerror.argtypes = [i32]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        for fn in (lib.fa_fwd, lib.fa_decode_split, lib.fa_combine, lib.fa_decode_num_splits,
+                   lib.fa_fwd_tile_shape):
+            fn.restype = i32
+        _lib = lib
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return library().fa_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != FA_OK:
+        raise FAError(fn, status)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_ptr(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on a HIP device (got %s); the library has no CPU path" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions (got shape %s)" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fa_fwd.  q [B,H,N_q,d], k/v [B,H_kv,N_k,d] bf16 -> o [B,H,N_q,d] bf16, lse [B,H,N_q] fp32."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, H, N_q, d = q.shape
+    Bk, H_kv, N_k, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, N_q):
+        raise ValueError("output shapes do not match q")
+    _check("fa_fwd", library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      B, H, H_kv, N_q, N_k, d, int(bool(causal)), float(scale), _stream_ptr(q)))
+    return out, lse
+
+
+def decode_split(q, k, v, num_splits: int, scale: float | None = None, o_part=None, lse_part=None):
+    """fa_decode_split.  q [B,H,d], k/v [B,H_kv,N_k,d] bf16 -> o_part [B,H,S,d], lse_part [B,H,S] fp32."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, H, d = q.shape
+    Bk, H_kv, N_k, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    S = int(num_splits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o_part is None:
+        o_part = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32, 4)
+    _need(lse_part, "lse_part", torch.float32, 3)
+    if tuple(o_part.shape) != (B, H, S, d) or tuple(lse_part.shape) != (B, H, S):
+        raise ValueError("partial output shapes do not match")
+    _check("fa_decode_split",
+           library().fa_decode_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+                                     lse_part.data_ptr(), B, H, H_kv, N_k, d, S, float(scale), _stream_ptr(q)))
+    return o_part, lse_part
+
+
+def combine(o_part, lse_part, out=None, lse=None):
+    """fa_combine.  o_part [B,H,S,d], lse_part [B,H,S] fp32 -> o [B,H,d] bf16, lse [B,H] fp32."""
+    torch = _torch()
+    _need(o_part, "o_part", torch.float32, 4)
+    _need(lse_part, "lse_part", torch.float32, 3)
+    B, H, S, d = o_part.shape
+    if tuple(lse_part.shape) != (B, H, S):
+        raise ValueError("lse_part shape does not match o_part")
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.bfloat16, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=o_part.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    _check("fa_combine", library().fa_combine(o_part.data_ptr(), lse_part.data_ptr(), out.data_ptr(),
+                                              lse.data_ptr(), B, H, d, S, _stream_ptr(o_part)))
+    return out, lse
+
+
+def decode(q, k, v, num_splits: int | None = None, scale: float | None = None):
+    """Split then combine on the current stream; returns (o [B,H,d] bf16, lse [B,H] fp32)."""
+    B, H, d = q.shape
+    if num_splits is None:
+        num_splits = decode_num_splits(B, k.shape[1], k.shape[2], d)
+    o_part, lse_part = decode_split(q, k, v, num_splits, scale)
+    return combine(o_part, lse_part)
+
+
+def decode_num_splits(B: int, H_kv: int, N_k: int, d: int) -> int:
+    return int(library().fa_decode_num_splits(B, H_kv, N_k, d))
+
+
+def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(library().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def fwd_tile_shape(d: int):
+    r, c = ctypes.c_int(), ctypes.c_int()
+    _check("fa_fwd_tile_shape", library().fa_fwd_tile_shape(d, ctypes.byref(r), ctypes.byref(c)))
+    return r.value, c.value
+
+
+def fwd_tile_count(N_q: int, N_k: int, d: int, causal: bool) -> int:
+    return int(library().fa_fwd_tile_count(N_q, N_k, d, int(bool(causal))))

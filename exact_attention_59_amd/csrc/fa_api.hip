@@ -1,0 +1,168 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument validation (before any
+// HIP call), dispatch to the gfx950 kernels, and the host-side helpers.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "fa.h"
+#include "fa_launch.hpp"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool debug_enabled() {
+    static const bool on = [] {
+        const char* v = getenv("FA_DEBUG");
+        return v && v[0] && v[0] != '0';
+    }();
+    return on;
+}
+
+int finish(hipError_t err, const char* what) {
+    if (err != hipSuccess) {
+        if (debug_enabled()) fprintf(stderr, "[fa] %s launch failed: %s\n", what, hipGetErrorString(err));
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
+// Largest element count of one tensor we accept (offsets are 64-bit inside the kernels;
+// grid sizes are checked separately).
+constexpr long long kMaxElems = 1LL << 62;
+
+int compute_units() {
+    static std::once_flag once;
+    static int cus = 256;
+    std::call_once(once, [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        (void)hipGetLastError();  // a machine without a GPU leaves an error behind; clear it
+    });
+    return cus;
+}
+
+}  // namespace
+
+FA_EXPORT const char* fa_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "success";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "invalid shape (a size <= 0, H not a multiple of H_kv, or num_splits outside [1, N_k])";
+        case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dimension must be 64 or 128, or a size exceeds the limits)";
+        case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case FA_ERR_ARG: return "invalid argument (scale not finite, or causal not 0/1)";
+        case FA_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
+        default: return "unknown status";
+    }
+}
+
+FA_EXPORT int fa_fwd_tile_shape(int d, int* block_rows, int* block_cols) {
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (block_rows) *block_rows = fa::kFwdBlockRows;
+    if (block_cols) *block_cols = fa::kFwdBlockCols;
+    return FA_OK;
+}
+
+// Mirrors the kernel's loop bounds: query tile i walks key tiles 0 .. n_i - 1, where
+// n_i stops at the last key visible to the tile's last real row.
+FA_EXPORT long long fa_fwd_tile_count(int N_q, int N_k, int d, int causal) {
+    if (N_q <= 0 || N_k <= 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1)) return -1;
+    const long long BR = fa::kFwdBlockRows, BC = fa::kFwdBlockCols;
+    const long long T_r = (N_q + BR - 1) / BR, T_c = (N_k + BC - 1) / BC;
+    if (!causal) return T_r * T_c;
+    long long total = 0;
+    for (long long i = 0; i < T_r; ++i) {
+        const long long last_row = (i * BR + BR < N_q ? i * BR + BR : N_q) - 1;
+        const long long kl = last_row + (N_k - N_q);
+        if (kl >= 0) total += (kl / BC + 1 < T_c) ? kl / BC + 1 : T_c;
+    }
+    return total;
+}
+
+FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
+                     int N_q, int N_k, int d, int causal, float scale, void* stream) {
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_q <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
+    if (H % H_kv) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * N_q * d >= kMaxElems || (long long)B * H_kv * N_k * d >= kMaxElems)
+        return FA_ERR_UNSUPPORTED;
+    const long long blocks = (long long)((N_q + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * H;
+    if (blocks > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(LSE)) return FA_ERR_ALIGN;
+    if (!isfinite(scale)) return FA_ERR_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] fwd B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d causal=%d blocks=%lld\n", B, H, H_kv, N_q,
+                N_k, d, causal, blocks);
+    return finish(fa::launch_fwd(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal == 1, scale,
+                                 static_cast<hipStream_t>(stream)),
+                  "fa_fwd");
+}
+
+FA_EXPORT int fa_decode_split(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
+                              int B, int H, int H_kv, int N_k, int d, int num_splits, float scale,
+                              void* stream) {
+    if (!Q || !K || !V || !O_part || !LSE_part) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
+    if (H % H_kv) return FA_ERR_SHAPE;
+    if (num_splits < 1 || num_splits > N_k) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (H / H_kv > 4 * fa::kDecHeadsPerBlock) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H_kv * N_k * d >= kMaxElems || (long long)B * H * num_splits * d >= kMaxElems)
+        return FA_ERR_UNSUPPORTED;
+    const long long n_qc = (H / H_kv + fa::kDecHeadsPerBlock - 1) / fa::kDecHeadsPerBlock;
+    if ((long long)num_splits * n_qc * B * H_kv > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O_part) || misaligned(LSE_part))
+        return FA_ERR_ALIGN;
+    if (!isfinite(scale)) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] decode_split B=%d H=%d H_kv=%d N_k=%d d=%d S=%d\n", B, H, H_kv, N_k, d, num_splits);
+    return finish(fa::launch_decode_split(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, d, num_splits, scale,
+                                          static_cast<hipStream_t>(stream)),
+                  "fa_decode_split");
+}
+
+FA_EXPORT int fa_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H, int d,
+                         int num_splits, void* stream) {
+    if (!O_part || !LSE_part || !O) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || d <= 0 || num_splits < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * num_splits * d >= kMaxElems || (long long)B * H > 0x7fffffffLL)
+        return FA_ERR_UNSUPPORTED;
+    if (misaligned(O_part) || misaligned(LSE_part) || misaligned(O) || (LSE && misaligned(LSE)))
+        return FA_ERR_ALIGN;
+    if (debug_enabled()) fprintf(stderr, "[fa] combine B=%d H=%d d=%d S=%d\n", B, H, d, num_splits);
+    return finish(fa::launch_combine(O_part, LSE_part, O, LSE, B, H, d, num_splits,
+                                     static_cast<hipStream_t>(stream)),
+                  "fa_combine");
+}
+
+// Split count: aim for about two resident workgroups per compute unit in one wave of
+// workgroups, but keep every segment at least 256 keys long (Lecture 11 section 6.4).
+FA_EXPORT int fa_decode_num_splits(int B, int H_kv, int N_k, int d) {
+    if (B <= 0 || H_kv <= 0 || N_k <= 0 || d <= 0) return 0;
+    const long long heads = (long long)B * H_kv;
+    const long long target = 2LL * compute_units();
+    long long s = (target + heads - 1) / heads;
+    const long long max_by_len = N_k / 256 > 0 ? N_k / 256 : 1;
+    if (s > max_by_len) s = max_by_len;
+    if (s < 1) s = 1;
+    if (s > N_k) s = N_k;
+    return (int)s;
+}
+
+FA_EXPORT size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+    if (B <= 0 || H <= 0 || d <= 0 || num_splits <= 0) return 0;
+    const size_t rows = (size_t)B * H * num_splits;
+    return rows * (size_t)d * sizeof(float) + rows * sizeof(float);
+}

@@ -1,0 +1,69 @@
+// fa_common.hpp -- device-side building blocks shared by the gfx950 attention kernels:
+// vector types, the two bf16 MFMA shapes used, lane reductions, bf16 packing.
+//
+// MFMA register layouts relied on (CDNA3/CDNA4 matrix-core conventions, 64-lane wave):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l % 32][8*(l/32) + e], e = 0..7
+//     B: lane l holds B[8*(l/32) + e][l % 32]
+//     D: lane l, register r holds D[8*(r/4) + 4*(l/32) + r%4][l % 32]
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds A[l % 16][8*(l/16) + e]
+//     B: lane l holds B[8*(l/16) + e][l % 16]
+//     D: lane l, register r holds D[4*(l/16) + r][l % 16]
+// The contraction index only has to be numbered the same way in A and B, so the
+// kernels are free to permute it (they do, to make loads contiguous).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLn2 = 0.693147180559945309417f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exact at x = 0, 0 at -inf.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the transcendental unit (v_log_f32).
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, kWave)); }
+__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, kWave); }
+
+// Round two floats to bf16 (RNE, v_cvt_pk_bf16_f32) and pack them, lo first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// bf16 (raw bits) -> float, exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Order LDS traffic of one wave: every lane's earlier LDS accesses complete before
+// any later one is issued, and the compiler may not move LDS accesses across it.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace fa

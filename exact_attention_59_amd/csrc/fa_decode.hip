@@ -1,0 +1,340 @@
+// fa_decode.hip -- flash-decoding for gfx950: split-KV kernel and log-sum-exp combine.
+//
+// What is computed (Lecture 11 sections 6.1-6.4): one query token per sequence.  The
+// cached keys are cut into S contiguous segments (views, no copy); a workgroup per
+// (sequence, key/value head, segment) runs the online softmax over its segment and
+// writes the segment's normalised output o_s and lse_s; the combine kernel merges the
+// segments exactly: lse = log sum_s e^(lse_s), o = sum_s e^(lse_s - lse) o_s.
+//
+// Split kernel design (HBM-bound: every K/V byte is read exactly once):
+//   - the H/H_kv query heads sharing a key/value head are packed as the N columns of
+//     one MFMA tile (up to 16 per workgroup), so K and V are read once per group
+//     (Lecture 11 section 6.2, GQA packing into the M dimension of the tile);
+//   - the 4 waves of a workgroup take interleaved 32-key blocks of the segment and
+//     keep independent online states; they are merged once at the end through LDS.
+//     Waves never wait for each other inside the key loop;
+//   - each wave loads its next block into registers while it computes the current
+//     one (about 16 KB in flight per wave at d = 128);
+//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane holds one query (lane % 16)
+//     and 8 of every 32 keys; K comes straight from global memory in A-operand layout
+//     (each lane reads 64 contiguous bytes of one key row per 16-key block; the head
+//     dimension is permuted inside the contraction to make that possible);
+//   - O^T += V^T P^T needs V transposed: each wave writes its V block to its own LDS
+//     region as Vt[d][key] and reads it back in the permuted key order of P^T.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+namespace {
+
+template <int D>
+struct DecCfg {
+    static constexpr int KB = kDecKeysPerWave;    // keys per wave iteration
+    static constexpr int NQ = kDecHeadsPerBlock;  // query heads per workgroup (MFMA N)
+    static constexpr int NW = 4;
+    static constexpr int VS = KB + 8;              // LDS row stride (elements) of Vt [D][KB]
+    static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    static constexpr int V_KPT = KB * CPR / 64;    // V keys per lane (one chunk each)
+    static constexpr int KSTEPS = D / 32;          // contraction steps of S^T
+    static_assert(64 / CPR * V_KPT == KB, "V transpose mapping must cover the block");
+    static_assert(V_KPT % 2 == 0, "keys per lane must pair up");
+    static constexpr int VT_ELEMS = NW * D * VS;                  // per-wave transposed V blocks
+    static constexpr int MERGE_FLOATS = NW * NQ * (D + 2);        // per-wave (m, l, acc)
+    static constexpr int SMEM_BYTES =
+        (VT_ELEMS * 2 > MERGE_FLOATS * 4) ? VT_ELEMS * 2 : MERGE_FLOATS * 4;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __restrict__ Q,
+                                                              const uint16_t* __restrict__ K,
+                                                              const uint16_t* __restrict__ V,
+                                                              float* __restrict__ O_part,
+                                                              float* __restrict__ LSE_part, int H,
+                                                              int H_kv, int N_k, int S, int L, int n_qc,
+                                                              float c) {
+    using C = DecCfg<D>;
+    constexpr int KB = C::KB, NQ = C::NQ, NW = C::NW, VS = C::VS, CPR = C::CPR;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n16 = lane & 15, hq = lane >> 4;
+
+    int bid = blockIdx.x;
+    const int s = bid % S;
+    bid /= S;
+    const int qc = bid % n_qc;
+    const int bg = bid / n_qc;  // b * H_kv + g
+    const int group = H / H_kv;
+    const int b = bg / H_kv, g = bg - b * H_kv;
+
+    const int k_beg = min(s * L, N_k), k_end = min(k_beg + L, N_k);
+    const int nblk = (k_end - k_beg + KB - 1) / KB;
+    const int64_t kv_base = (int64_t)bg * N_k * D;
+
+    // Query head of this lane's MFMA column.
+    const int qh = qc * NQ + n16;  // index inside the group
+    const bool q_valid = qh < group;
+    const int h = g * group + qh;
+
+    // Q fragment (B operand): lane holds Q[h][(D/4)*hq + 8*t + e] for step t (the head
+    // dimension is permuted inside the contraction so each lane reads contiguous bytes).
+    bf16x8 qf[C::KSTEPS];
+    if (q_valid) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(Q + ((int64_t)b * H + h) * D + (D / 4) * hq);
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(qp[t]);
+    } else {
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+
+    uint16_t* Vt = reinterpret_cast<uint16_t*>(smem) + w * D * VS;
+
+    // Per-wave block staging: K in A-operand layout, V as row chunks for the transpose.
+    u32x4 kreg[2][C::KSTEPS], vreg[C::V_KPT];
+    const int v_dc = lane % CPR, v_kg = lane / CPR;
+    auto load_block = [&](int bi) {
+        const int key0 = k_beg + bi * KB;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int key = key0 + 16 * mb + n16;
+            const int key_c = min(key, N_k - 1);  // in-bounds address; the value is zeroed below
+            const u32x4* kp = reinterpret_cast<const u32x4*>(K + kv_base + (int64_t)key_c * D + (D / 4) * hq);
+#pragma unroll
+            for (int t = 0; t < C::KSTEPS; ++t) kreg[mb][t] = key < k_end ? kp[t] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int r = 0; r < C::V_KPT; ++r) {
+            const int key = key0 + v_kg * C::V_KPT + r;
+            const int key_c = min(key, N_k - 1);
+            vreg[r] = key < k_end ? *reinterpret_cast<const u32x4*>(V + kv_base + (int64_t)key_c * D + v_dc * 8)
+                                  : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    float m2 = -INFINITY, lsum = 0.f;
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
+
+    if (w < nblk) load_block(w);
+    for (int bi = w; bi < nblk; bi += NW) {
+        u32x4 kcur[2][C::KSTEPS], vcur[C::V_KPT];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int t = 0; t < C::KSTEPS; ++t) kcur[mb][t] = kreg[mb][t];
+#pragma unroll
+        for (int r = 0; r < C::V_KPT; ++r) vcur[r] = vreg[r];
+        if (bi + NW < nblk) load_block(bi + NW);
+
+        // V block -> this wave's LDS region, transposed to Vt[d][key].
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t words[C::V_KPT / 2];
+#pragma unroll
+            for (int p = 0; p < C::V_KPT / 2; ++p) {
+                const uint32_t a = vcur[2 * p][e >> 1], bb = vcur[2 * p + 1][e >> 1];
+                words[p] = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
+            }
+            uint16_t* dst = Vt + (v_dc * 8 + e) * VS + v_kg * C::V_KPT;
+            if constexpr (C::V_KPT == 8) {
+                *reinterpret_cast<u32x4*>(dst) = u32x4{words[0], words[1], words[2], words[3]};
+            } else {
+                static_assert(C::V_KPT == 4, "unsupported V keys per lane");
+                *reinterpret_cast<u32x2*>(dst) = u32x2{words[0], words[1]};
+            }
+        }
+        wave_lds_fence();
+
+        // S^T[key][query] for two 16-key blocks.
+        f32x4 sc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            sc[mb] = f32x4{};
+#pragma unroll
+            for (int t = 0; t < C::KSTEPS; ++t) sc[mb] = mfma16(as_bf16x8(kcur[mb][t]), qf[t], sc[mb]);
+        }
+        // Mask keys past the segment (only the last block can be short).
+        const int key0 = k_beg + bi * KB;
+        if (key0 + KB > k_end) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (key0 + 16 * mb + 4 * hq + r >= k_end) sc[mb][r] = -INFINITY;
+        }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[mb][r]);
+        mx = xor_max(xor_max(mx, 16), 32);
+        const float m_new = fmaxf(m2, mx * c);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_hw(m2 - m_use);
+        float ps = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2_hw(fmaf(sc[mb][r], c, -m_use));
+                sc[mb][r] = p;
+                ps += p;
+            }
+        ps = xor_sum(xor_sum(ps, 16), 32);
+        lsum = fmaf(lsum, alpha, ps);
+        m2 = m_new;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
+
+        // P^T as B operand: slot e <-> key 16*(e/4) + 4*hq + e%4.
+        const bf16x8 pf = as_bf16x8(u32x4{pack_bf16x2(sc[0][0], sc[0][1]), pack_bf16x2(sc[0][2], sc[0][3]),
+                                          pack_bf16x2(sc[1][0], sc[1][1]), pack_bf16x2(sc[1][2], sc[1][3])});
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const uint16_t* vp = Vt + (16 * db + n16) * VS + 4 * hq;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
+            acc[db] = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf, acc[db]);
+        }
+        wave_lds_fence();  // all lanes' reads of Vt done before the next block overwrites it
+    }
+
+    // Merge the 4 wave states through LDS (reusing the Vt space).
+    __syncthreads();
+    float* mm = reinterpret_cast<float*>(smem);  // [NW][NQ]
+    float* ll = mm + NW * NQ;                    // [NW][NQ]
+    float* aa = ll + NW * NQ;                    // [NW][NQ][D]
+    if (hq == 0) {
+        mm[w * NQ + n16] = m2;
+        ll[w * NQ + n16] = lsum;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) aa[(w * NQ + n16) * D + 16 * db + 4 * hq + r] = acc[db][r];
+    __syncthreads();
+
+    // 256 threads x (D/16) outputs: thread -> query n = tid / 16, d chunk tid % 16.
+    constexpr int DPT = D / 16;
+    const int n = tid >> 4, d0 = (tid & 15) * DPT;
+    const int qh_out = qc * NQ + n;
+    if (qh_out < group) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) M = fmaxf(M, mm[v * NQ + n]);
+        const int64_t row = ((int64_t)b * H + (g * group + qh_out)) * S + s;
+        float o[DPT];
+        float lse;
+        if (M == -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < DPT; ++k) o[k] = 0.f;
+            lse = -INFINITY;
+        } else {
+            float wt[NW], l = 0.f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const float mv = mm[v * NQ + n];
+                wt[v] = mv == -INFINITY ? 0.f : exp2_hw(mv - M);
+                l = fmaf(wt[v], ll[v * NQ + n], l);
+            }
+            const float inv = 1.f / l;
+#pragma unroll
+            for (int k = 0; k < DPT; ++k) {
+                float x = 0.f;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) x = fmaf(wt[v], aa[(v * NQ + n) * D + d0 + k], x);
+                o[k] = x * inv;
+            }
+            lse = (M + log2_hw(l)) * kLn2;
+        }
+        float4* op = reinterpret_cast<float4*>(O_part + row * D + d0);
+#pragma unroll
+        for (int k = 0; k < DPT / 4; ++k) op[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+        if ((tid & 15) == 0) LSE_part[row] = lse;
+    }
+}
+
+// One wave per (b, h): lse = M + ln sum_s e^(lse_s - M); O = sum_s e^(lse_s - lse) o_s.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O_part,
+                                                      const float* __restrict__ LSE_part,
+                                                      uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                                      int BH, int S) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr int DPL = D / 64;  // outputs per lane
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= BH) return;
+    const float* lp = LSE_part + (int64_t)row * S;
+    float M = -INFINITY;
+    for (int t = lane; t < S; t += 64) M = fmaxf(M, lp[t]);
+    for (int k = 32; k >= 1; k >>= 1) M = xor_max(M, k);
+    float o[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+        float sum = 0.f;
+        for (int t = lane; t < S; t += 64) sum += exp2_hw((lp[t] - M) * kLog2e);
+        for (int k = 32; k >= 1; k >>= 1) sum = xor_sum(sum, k);
+        lse = M + log2_hw(sum) * kLn2;
+        const float* op = O_part + (int64_t)row * S * D + lane * DPL;
+        for (int t = 0; t < S; ++t) {
+            const float wgt = exp2_hw((lp[t] - lse) * kLog2e);  // 0 for an empty segment
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) o[k] = fmaf(wgt, op[(int64_t)t * D + k], o[k]);
+        }
+    }
+    uint16_t* dst = O + (int64_t)row * D + lane * DPL;
+    if constexpr (DPL == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o[0], o[1]);
+    } else {
+        const uint32_t pk = pack_bf16x2(o[0], 0.f);
+        *dst = (uint16_t)(pk & 0xffffu);
+    }
+    if (LSE && lane == 0) LSE[row] = lse;
+}
+
+template <int D>
+hipError_t launch_decode_t(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
+                           int B, int H, int H_kv, int N_k, int S, float scale, hipStream_t stream) {
+    const int group = H / H_kv;
+    const int n_qc = (group + kDecHeadsPerBlock - 1) / kDecHeadsPerBlock;
+    const int L = (N_k + S - 1) / S;
+    const float c = (float)((double)scale * 1.4426950408889634073599);
+    const long long blocks = (long long)S * n_qc * B * H_kv;
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                       static_cast<const uint16_t*>(V), O_part, LSE_part, H, H_kv, N_k, S, L, n_qc, c);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_combine_t(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,
+                            int S, hipStream_t stream) {
+    const int BH = B * H;
+    hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream, O_part,
+                       LSE_part, static_cast<uint16_t*>(O), LSE, BH, S);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_split(const void* Q, const void* K, const void* V, float* O_part,
+                               float* LSE_part, int B, int H, int H_kv, int N_k, int d, int num_splits,
+                               float scale, hipStream_t stream) {
+    if (d == 64)
+        return launch_decode_t<64>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale, stream);
+    return launch_decode_t<128>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale, stream);
+}
+
+hipError_t launch_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,
+                          int d, int num_splits, hipStream_t stream) {
+    if (d == 64) return launch_combine_t<64>(O_part, LSE_part, O, LSE, B, H, num_splits, stream);
+    return launch_combine_t<128>(O_part, LSE_part, O, LSE, B, H, num_splits, stream);
+}
+
+}  // namespace fa

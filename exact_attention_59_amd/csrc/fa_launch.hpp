@@ -1,0 +1,29 @@
+// fa_launch.hpp -- library-internal launchers (C++ linkage, hidden); fa_api.hip calls them
+// after validating arguments.  Each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Forward tile shape (query rows per workgroup, keys per tile); both head dimensions
+// use the same shape.
+constexpr int kFwdBlockRows = 128;
+constexpr int kFwdBlockCols = 64;
+
+// Decode: keys per wave iteration and query heads per workgroup.
+constexpr int kDecKeysPerWave = 32;
+constexpr int kDecHeadsPerBlock = 16;
+
+hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                      int H_kv, int N_q, int N_k, int d, bool causal, float scale, hipStream_t stream);
+
+hipError_t launch_decode_split(const void* Q, const void* K, const void* V, float* O_part,
+                               float* LSE_part, int B, int H, int H_kv, int N_k, int d, int num_splits,
+                               float scale, hipStream_t stream);
+
+hipError_t launch_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,
+                          int d, int num_splits, hipStream_t stream);
+
+}  // namespace fa

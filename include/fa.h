@@ -1,0 +1,133 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact attention on AMD Instinct MI355X (gfx950).
+ *
+ * Three compute entry points:
+ *   fa_fwd           FlashAttention-2 forward: O = softmax(scale * Q K^T) V and the
+ *                    per-row log-sum-exp, computed tile by tile with the online
+ *                    softmax state (m, l, acc); S and P never reach device memory.
+ *   fa_decode_split  flash-decoding, step 2: one query token per sequence, keys cut
+ *                    into num_splits contiguous segments, per-segment normalised
+ *                    output o_s and lse_s.
+ *   fa_combine       flash-decoding, step 3: exact merge of the segments by
+ *                    log-sum-exp.
+ * Sources: Lecture 11, "Kernel Optimization Techniques: FlashAttention,
+ * flash-decoding and megakernel", sections 2-6; the FlashAttention v1 and v2
+ * cards of the "CUDA Kernel interview course" page.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers (hipMalloc'd or equivalent), except where a
+ *     parameter says otherwise.  The caller allocates and frees every buffer;
+ *     the library allocates nothing and keeps no state besides a cached
+ *     compute-unit count.
+ *   - bf16 tensors are raw 16-bit bfloat16 storage (1 sign, 8 exponent, 7
+ *     mantissa bits), passed as void*.  All tensors are dense, row-major, with
+ *     the innermost dimension contiguous, and start on a 16-byte boundary.
+ *     Outputs must not overlap inputs.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Calls are asynchronous: they enqueue work and return.  A launch failure
+ *     reported by the HIP runtime returns FA_ERR_HIP; faults during execution
+ *     surface at the caller's next synchronisation of the stream.
+ *   - Arguments are validated before any HIP call.  On any error status the
+ *     outputs are left untouched and nothing is enqueued.
+ *   - Entry points are thread-safe and re-entrant.
+ *   - Scores are scale * (q . k); LSE is the natural logarithm of the sum of
+ *     exp(score) over the visible keys.  A row with no visible key gets O = 0
+ *     and LSE = -inf.  NaN or Inf inputs propagate; they are not detected.
+ *   - Query head h reads key/value head h / (H / H_kv) (contiguous groups).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,       /* a size is <= 0, H % H_kv != 0, or num_splits out of range */
+    FA_ERR_UNSUPPORTED = 3, /* head dimension d not in {64, 128}, or a size beyond the limits below */
+    FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+    FA_ERR_ARG = 5,         /* scale not finite, or causal not 0/1 */
+    FA_ERR_HIP = 6          /* the HIP runtime reported an error when enqueueing */
+} fa_status;
+
+/*
+ * Exact attention forward (FlashAttention-2 order: one workgroup per query tile,
+ * K/V tiles streamed through LDS; Lecture 11 sections 4.1-4.2 and 5.3; the v2
+ * card's work partitioning).
+ *   Q   [B][H][N_q][d]    bf16, read
+ *   K   [B][H_kv][N_k][d] bf16, read
+ *   V   [B][H_kv][N_k][d] bf16, read
+ *   O   [B][H][N_q][d]    bf16, written (round-to-nearest-even)
+ *   LSE [B][H][N_q]       fp32, written (natural log)
+ *   causal: 0 = no mask; 1 = bottom-right aligned causal mask, query i sees key j
+ *           iff j <= i + N_k - N_q (the lower triangle when N_q == N_k).
+ *   scale: multiplies q . k (usually 1/sqrt(d)); must be finite.
+ * Limits: d in {64, 128}; B*H*N_q*d and B*H_kv*N_k*d below 2^62.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
+           int N_q, int N_k, int d, int causal, float scale, void* stream);
+
+/*
+ * Flash-decoding split step (Lecture 11 section 6.2, steps 1-2): one query token
+ * per sequence; the N_k cached keys are cut into num_splits contiguous segments of
+ * L = ceil(N_k / num_splits) keys (the last ones may be short or empty).  The
+ * H / H_kv query heads that share a key/value head are processed together, so
+ * each K/V element is read once.  No causal mask (the single query sees every
+ * cached key).
+ *   Q        [B][H][d]               bf16, read
+ *   K, V     [B][H_kv][N_k][d]       bf16, read
+ *   O_part   [B][H][num_splits][d]   fp32, written: o_s, normalised within the segment
+ *   LSE_part [B][H][num_splits]      fp32, written: lse_s (natural log); -inf and
+ *                                     o_s = 0 for an empty segment
+ * num_splits must lie in [1, N_k].  fa_decode_num_splits gives a default.
+ * Limits: d in {64, 128}; H / H_kv <= 64.
+ */
+int fa_decode_split(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
+                    int B, int H, int H_kv, int N_k, int d, int num_splits, float scale, void* stream);
+
+/*
+ * Flash-decoding combine (Lecture 11 section 6.2, step 3): per (b, h),
+ *   lse = log sum_s exp(lse_s),  O = sum_s exp(lse_s - lse) o_s,
+ * evaluated with the largest lse_s subtracted first.  If every segment is empty,
+ * O = 0 and LSE = -inf.
+ *   O_part [B][H][num_splits][d] fp32 and LSE_part [B][H][num_splits] fp32, read
+ *   O      [B][H][d]  bf16, written
+ *   LSE    [B][H]     fp32, written (may be NULL if not wanted)
+ */
+int fa_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,
+               int d, int num_splits, void* stream);
+
+/*
+ * Default split count for fa_decode_split (Lecture 11 section 6.4: enough
+ * workgroups to fill the compute units, segments not so short that fixed
+ * costs dominate).  Host-only; queries the current device's compute-unit count
+ * once (256 is assumed when no device is visible).  Returns a value in
+ * [1, N_k], or 0 if an argument is <= 0.
+ */
+int fa_decode_num_splits(int B, int H_kv, int N_k, int d);
+
+/* Bytes of O_part plus LSE_part for the given shape (host-only, no HIP call);
+ * 0 if an argument is <= 0. */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/* Query-tile rows (B_r) and key-tile columns (B_c) that fa_fwd uses for head
+ * dimension d; returns FA_OK, or FA_ERR_UNSUPPORTED.  Host-only. */
+int fa_fwd_tile_shape(int d, int* block_rows, int* block_cols);
+
+/* Number of (query tile, key tile) pairs fa_fwd computes for one (b, h) -- the
+ * causal schedule skips tiles that are entirely masked (Lecture 11 section 5.3).
+ * Host-only; -1 on a bad argument. */
+long long fa_fwd_tile_count(int N_q, int N_k, int d, int causal);
+
+/* Static description of a status code.  Never NULL. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

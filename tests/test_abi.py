@@ -1,0 +1,135 @@
+"""The C ABI of libfa.so without a GPU: exports, validation statuses, host helpers.
+
+Every compute call made here is invalid on purpose, so it returns from argument
+validation before any HIP call; nothing is enqueued and no pointer is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+fa = pytest.importorskip("exact_attention_59_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        from exact_attention_59_amd import build
+
+        build.build()
+    return fa.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def exported_symbols(path):
+    out = os.popen("nm -D --defined-only %s" % path).read()
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("fa_fwd", "fa_decode_split", "fa_combine", "fa_decode_num_splits",
+                 "fa_decode_workspace_bytes", "fa_strerror", "fa_fwd_tile_shape", "fa_fwd_tile_count"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    exported = exported_symbols(fa.library_path())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+    # nothing else of ours leaks out of the library
+    ours = {s for s in exported if s.startswith("fa_")}
+    assert ours == set(declared_functions())
+
+
+P = ctypes.c_void_p(0x100000)       # aligned, never dereferenced (validation fails first)
+P_MIS = ctypes.c_void_p(0x100004)   # 4-byte aligned only
+
+
+def fwd(lib, Q=P, K=P, V=P, O=P, L=P, B=1, H=1, H_kv=1, N_q=8, N_k=8, d=64, causal=0, scale=0.125):
+    return lib.fa_fwd(Q, K, V, O, L, B, H, H_kv, N_q, N_k, d, causal, scale, None)
+
+
+def dec(lib, Q=P, K=P, V=P, Op=P, Lp=P, B=1, H=4, H_kv=1, N_k=64, d=128, S=4, scale=0.1):
+    return lib.fa_decode_split(Q, K, V, Op, Lp, B, H, H_kv, N_k, d, S, scale, None)
+
+
+def comb(lib, Op=P, Lp=P, O=P, L=P, B=1, H=4, d=128, S=4):
+    return lib.fa_combine(Op, Lp, O, L, B, H, d, S, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(K=None), fa.FA_ERR_NULL), (dict(V=None), fa.FA_ERR_NULL),
+    (dict(O=None), fa.FA_ERR_NULL), (dict(L=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=-1), fa.FA_ERR_SHAPE), (dict(H_kv=0), fa.FA_ERR_SHAPE),
+    (dict(N_q=0), fa.FA_ERR_SHAPE), (dict(N_k=0), fa.FA_ERR_SHAPE), (dict(d=0), fa.FA_ERR_SHAPE),
+    (dict(H=6, H_kv=4), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(Q=P_MIS), fa.FA_ERR_ALIGN), (dict(O=P_MIS), fa.FA_ERR_ALIGN), (dict(L=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(scale=float("inf")), fa.FA_ERR_ARG), (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(causal=2), fa.FA_ERR_ARG), (dict(causal=-1), fa.FA_ERR_ARG),
+])
+def test_fwd_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(Op=None), fa.FA_ERR_NULL), (dict(Lp=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(N_k=-5), fa.FA_ERR_SHAPE), (dict(H=5, H_kv=2), fa.FA_ERR_SHAPE),
+    (dict(S=0), fa.FA_ERR_SHAPE), (dict(S=65), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED), (dict(H=65, H_kv=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(K=P_MIS), fa.FA_ERR_ALIGN), (dict(Lp=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(scale=float("-inf")), fa.FA_ERR_ARG),
+])
+def test_decode_validation(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Op=None), fa.FA_ERR_NULL), (dict(O=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(S=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(O=P_MIS), fa.FA_ERR_ALIGN), (dict(L=P_MIS), fa.FA_ERR_ALIGN),
+])
+def test_combine_validation(lib, kw, status):
+    assert comb(lib, **kw) == status
+
+
+def test_strerror_covers_every_status(lib):
+    texts = {fa.strerror(s) for s in range(7)}
+    assert len(texts) == 7
+    assert fa.strerror(99) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert fa.decode_workspace_bytes(4, 32, 128, 16) == 4 * 32 * 16 * (128 + 1) * 4
+    assert fa.decode_workspace_bytes(0, 32, 128, 16) == 0
+    assert fa.decode_workspace_bytes(1, 1, 64, -1) == 0
+
+
+def test_num_splits_range(lib):
+    for (B, H_kv, N_k) in [(4, 8, 4096), (4, 8, 65536), (1, 1, 1), (1, 2, 300), (64, 8, 2048), (256, 8, 128)]:
+        s = fa.decode_num_splits(B, H_kv, N_k, 128)
+        assert 1 <= s <= N_k
+        assert -(-N_k // s) >= min(N_k, 256) or s == 1  # segments are not shorter than 256 keys
+    assert fa.decode_num_splits(0, 8, 4096, 128) == 0
+    # more sequences need fewer splits (wave quantisation, Lecture 11 section 6.4)
+    assert fa.decode_num_splits(1, 8, 65536, 128) >= fa.decode_num_splits(16, 8, 65536, 128)
+
+
+def test_tile_shape(lib):
+    assert fa.fwd_tile_shape(64) == fa.fwd_tile_shape(128)
+    br, bc = fa.fwd_tile_shape(128)
+    assert br % 32 == 0 and bc % 32 == 0
+    with pytest.raises(fa.FAError):
+        fa.fwd_tile_shape(96)

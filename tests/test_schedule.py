@@ -1,0 +1,60 @@
+"""The causal tile schedule (host helper mirroring the kernel's loop bounds)."""
+import json
+import os
+
+import pytest
+
+fa = pytest.importorskip("exact_attention_59_amd")
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(fa.library_path()):
+        from exact_attention_59_amd import build
+
+        build.build()
+    return fa.library()
+
+
+def test_closed_form_matches_printed_fractions():
+    # Lecture 11 section 5.3 / Exercise 4: T(T+1)/2 of T^2 square tiles, i.e. 1/2 + 1/(2T).
+    g = json.load(open(os.path.join(GOLDEN, "lecture11_causal_fraction.json")))
+    for blk, printed in zip(g["blocks"], g["printed_fraction"]):
+        T = g["N"] // blk
+        assert abs((T * (T + 1) / 2) / T ** 2 - printed) <= g["tolerance"]
+        assert abs(0.5 + 1 / (2 * T) - printed) <= g["tolerance"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [128, 1024, 4095, 4096, 8192])
+def test_kernel_schedule_fraction(d, N):
+    # With B_c dividing B_r, query tile i needs (i+1)*B_r/B_c key tiles: the same
+    # 1/2 + 1/(2 T_r) fraction of the full T_r x T_c rectangle, T_r = N / B_r.
+    br, bc = fa.fwd_tile_shape(d)
+    T_r, T_c = -(-N // br), -(-N // bc)
+    full = fa.fwd_tile_count(N, N, d, False)
+    assert full == T_r * T_c
+    causal = fa.fwd_tile_count(N, N, d, True)
+    want = sum(min(T_c, (min((i + 1) * br, N) - 1) // bc + 1) for i in range(T_r))
+    assert causal == want
+    if N % br == 0:
+        assert abs(causal / full - (0.5 + 1 / (2 * T_r))) < 1e-12
+
+
+def test_schedule_at_lecture_example():
+    # N = 4096, 128-row query tiles: 0.516 of the tiles (Exercise 4 of Lecture 11).
+    br, _ = fa.fwd_tile_shape(128)
+    assert br == 128
+    frac = fa.fwd_tile_count(4096, 4096, 128, True) / fa.fwd_tile_count(4096, 4096, 128, False)
+    assert abs(frac - 0.516) < 5e-4
+
+
+def test_bottom_right_alignment_and_empty_rows():
+    # N_q < N_k: every query sees the prefix; N_q > N_k: early queries see nothing.
+    br, bc = fa.fwd_tile_shape(64)
+    assert fa.fwd_tile_count(1, 1000, 64, True) == -(-1000 // bc)
+    assert fa.fwd_tile_count(br, 10 * bc, 64, True) == 10
+    assert fa.fwd_tile_count(3 * br, 1, 64, True) == 1
+    assert fa.fwd_tile_count(0, 10, 64, True) == -1
