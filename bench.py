@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,decode] [--all]
+
+One step = fa_fwd over the batched-prefill workload (B=16, H=16, N_q=N_k=1024, d=64,
+bf16), once without and once with the causal mask.  `value` is that step's nominal
+FLOPs (4*B*H*N_q*N_k*d, halved under the causal mask) over its GPU time, in TFLOPS.
+The flash-decoding leg (B=4, H=32, H_kv=8, d=128, N_k = 4096 and 65536; split kernel
+then combine kernel) runs in the same invocation and is reported under "decode" in
+GB/s of K+V read once, against the 8 TB/s HBM peak; the 256 MB last-level cache is
+overwritten before every timed decode repetition so K/V come from HBM.
+
+Inputs are synthetic and seeded (counter-based SplitMix64 + Box-Muller, see gen/),
+already resident in device memory when timing starts.  GPU times come from HIP
+events recorded on the stream the kernels run on.  The fp64 oracle is timed on the
+host cores on a bounded sample of the same workload (cpu_baseline); it is a reported
+baseline, not a target.
+
+Prints one JSON line.  --gpus N with N > 1 exits with an explanation: this build
+measures one GPU's share only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attn fwd TFLOPS & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCES = ["fa_common.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_decode.hip"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_59_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dev_bf16(a):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def fwd_inputs(seed, B, H, H_kv, N, d):
+    import gen
+
+    return (gen.normal_bf16(seed, gen.TENSOR_Q, (B, H, N, d)), gen.normal_bf16(seed, gen.TENSOR_K, (B, H_kv, N, d)),
+            gen.normal_bf16(seed, gen.TENSOR_V, (B, H_kv, N, d)))
+
+
+def fwd_flops(B, H, N_q, N_k, d, causal):
+    f = 4.0 * B * H * N_q * N_k * d
+    return f / 2 if causal else f
+
+
+# ---------------------------------------------------------------------------------- legs
+def leg_forward(fa, torch, steps, warmup, B=16, H=16, H_kv=16, N=1024, d=64, seed=2):
+    """The step: fa_fwd non-causal then causal on one input batch."""
+    Q, K, V = fwd_inputs(seed, B, H, H_kv, N, d)
+    q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        fa.fwd(q, k, v, causal=False, out=o, lse=lse)
+        if ev:
+            ev[1].record(stream)
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nc = [e[0].elapsed_time(e[1]) for e in evs]
+    ca = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
+    f_nc, f_c = fwd_flops(B, H, N, N, d, False), fwd_flops(B, H, N, N, d, True)
+    return {
+        "step_ms": step_ms, "wall_ms_per_step": wall * 1e3 / steps,
+        "tflops": (f_nc + f_c) / (step_ms * 1e-3) / 1e12,
+        "noncausal": {"ms": sum(nc) / steps, "tflops": f_nc / (sum(nc) / steps * 1e-3) / 1e12},
+        "causal": {"ms": sum(ca) / steps, "tflops": f_c / (sum(ca) / steps * 1e-3) / 1e12},
+        "flops_noncausal": f_nc, "flops_causal": f_c,
+        "bytes_noncausal": 2.0 * (B * H * N * d * 2 + B * H_kv * N * d * 2) + 4.0 * B * H * N,
+    }
+
+
+def leg_forward_other(fa, torch, reps, name, seed, B, H, H_kv, N, d, causal):
+    Q, K, V = fwd_inputs(seed, B, H, H_kv, N, d)
+    q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    stream = torch.cuda.current_stream()
+    ev[0].record(stream)
+    for i in range(reps):
+        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    ms = sum(times) / reps
+    fl = fwd_flops(B, H, N, N, d, causal)
+    return {"workload": name, "ms": ms, "ms_min": times[0], "tflops": fl / (ms * 1e-3) / 1e12,
+            "pct_peak": 100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=None):
+    import gen
+
+    Q = gen.normal_bf16(seed, gen.TENSOR_Q, (B, H, d), 3.0)
+    K = gen.normal_bf16(seed, gen.TENSOR_K, (B, H_kv, N_k, d))
+    V = gen.normal_bf16(seed, gen.TENSOR_V, (B, H_kv, N_k, d))
+    q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
+    del K, V
+    S = num_splits or fa.decode_num_splits(B, H_kv, N_k, d)
+    o_part = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+    l_part = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    kv_bytes = 2.0 * B * H_kv * N_k * d * 2
+    # Overwrite the last-level cache (256 MB) before every timed repetition.
+    flush = torch.empty(640 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fa.decode_split(q, k, v, S, o_part=o_part, lse_part=l_part)
+        fa.combine(o_part, l_part, out=o, lse=lse)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for i in range(reps):
+        flush.fill_(float(i))
+        evs[i][0].record(stream)
+        fa.decode_split(q, k, v, S, o_part=o_part, lse_part=l_part)
+        evs[i][1].record(stream)
+        fa.combine(o_part, l_part, out=o, lse=lse)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    split = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    comb = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    both = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    ms = sum(split) / reps
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    return {"N_k": N_k, "num_splits": S, "split_us": ms * 1e3, "split_us_median": split[reps // 2] * 1e3,
+            "combine_us": sum(comb) / reps * 1e3, "end_to_end_us": sum(both) / reps * 1e3,
+            "split_GBs": gbs, "split_pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS,
+            "end_to_end_GBs": kv_bytes / (sum(both) / reps * 1e-3) / 1e9, "kv_bytes": kv_bytes}
+
+
+def leg_copy(torch, reps=5, mib=1024):
+    """A plain device copy of known size (calibrates the HBM byte counters)."""
+    a = torch.empty(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"copy_bytes_each_way": a.numel() * 4, "reps": reps}
+
+
+def cpu_baseline(target_s=12.0):
+    """The fp64 oracle on a bounded, time-calibrated sample of the prefill workload's rows."""
+    import numpy as np
+
+    import oracle
+
+    B, H, N, d = 16, 16, 1024, 64
+    Q, K, V = fwd_inputs(2, B, H, H, N, d)
+    orc = oracle.Oracle()
+    threads = oracle.host_threads()
+    rng = np.random.default_rng(0)
+    n = 2048
+    elapsed, rows_done, flops = 0.0, 0, 0.0
+    while True:
+        rows = rng.integers(0, B * H * N, size=n)
+        t0 = time.perf_counter()
+        orc.attention(Q, K, V, causal=False, rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        rows_done += n
+        flops += 4.0 * N * d * n
+        if elapsed >= target_s * 0.8 or rows_done >= B * H * N:
+            break
+        n = int(min(B * H * N - rows_done, max(n, n * (target_s - elapsed) / max(dt, 1e-3))))
+        if n <= 0:
+            break
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": "%d random rows of the non-causal B=16 H=16 N=1024 d=64 workload (%.1f s fp64, "
+                      "%.4f%% of one forward)" % (rows_done, elapsed, 100.0 * rows_done / (B * H * N)),
+            "seconds": elapsed}
+
+
+def traffic_from_counters(dominant_kernel_substr):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if the kernel is unchanged."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None, "kernels changed since the counters were taken"
+    k = c.get("kernels", {}).get(dominant_kernel_substr)
+    if not k:
+        return None, "dominant kernel not in the counter summary"
+    return k.get("hbm_bytes_per_launch"), "profiles/hbm_counters.json"
+
+
+# ---------------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--legs", default="fwd,decode,cpu", help="comma list of fwd, decode, cpu, copy")
+    ap.add_argument("--all", action="store_true", help="also time the long-sequence and GQA forward workloads")
+    ap.add_argument("--decode-reps", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU's share is the "
+              "single-GPU kernel at its real shape; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_59_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.library()
+    torch.cuda.set_device(0)
+    legs = set(args.legs.split(","))
+    out = {"metric": METRIC, "value": None, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "batched prefill B=16 H=16 H_kv=16 N_q=N_k=1024 d=64 bf16, step = non-causal + causal",
+                      "global_batch": 16, "seq_len": 1024, "heads": 16, "head_dim": 64, "parallelism": "single GPU"}}
+
+    if "copy" in legs:
+        log("copy leg", leg_copy(torch))
+
+    if "fwd" in legs:
+        log("forward leg: %d warmup + %d timed steps" % (args.warmup, args.steps))
+        r = leg_forward(fa, torch, args.steps, args.warmup)
+        out["value"] = round(r["tflops"], 2)
+        out["ms_per_step"] = round(r["step_ms"], 4)
+        out["pct_bf16_peak"] = round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2)
+        out["detail"] = {"noncausal_tflops": round(r["noncausal"]["tflops"], 1),
+                         "noncausal_us": round(r["noncausal"]["ms"] * 1e3, 2),
+                         "causal_tflops": round(r["causal"]["tflops"], 1),
+                         "causal_us": round(r["causal"]["ms"] * 1e3, 2),
+                         "wall_ms_per_step": round(r["wall_ms_per_step"], 4)}
+        achieved = r["flops_noncausal"] / (r["noncausal"]["ms"] * 1e-3) / 1e12
+        traffic, src = traffic_from_counters("fwd_kernel<64, false>")
+        out["roofline"] = {"kernel": "fwd_kernel<64, false> (non-causal, d=64)", "bound": "mfma",
+                           "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                           "traffic_source": src, "avg_launch_us": round(r["noncausal"]["ms"] * 1e3, 2),
+                           "algorithmic_flops_per_launch": r["flops_noncausal"],
+                           "algorithmic_bytes_per_launch": r["bytes_noncausal"]}
+        log("forward", out["detail"])
+
+    if "decode" in legs:
+        dec = {}
+        for N_k, seed in ((4096, 5), (65536, 6)):
+            log("decode leg N_k=%d" % N_k)
+            dec["N_k=%d" % N_k] = {k: (round(v, 2) if isinstance(v, float) else v)
+                                   for k, v in leg_decode(fa, torch, args.decode_reps, N_k, seed).items()}
+            log("decode", dec["N_k=%d" % N_k])
+            torch.cuda.empty_cache()
+        out["decode"] = dec
+
+    if args.all:
+        others = [("long causal B=2 H=16 N=8192 d=128", 3, 2, 16, 16, 8192, 128, True),
+                  ("GQA ragged causal B=4 H=32 H_kv=8 N=4095 d=128", 4, 4, 32, 8, 4095, 128, True),
+                  ("batched prefill B=16 H=16 N=1024 d=128 non-causal", 2, 16, 16, 16, 1024, 128, False)]
+        out["also_measured"] = []
+        for name, seed, B, H, H_kv, N, d, causal in others:
+            log("forward", name)
+            out["also_measured"].append({k: (round(v, 2) if isinstance(v, float) else v) for k, v in
+                                         leg_forward_other(fa, torch, 20, name, seed, B, H, H_kv, N, d,
+                                                           causal).items()})
+
+    if "cpu" in legs:
+        log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)
+        cb = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()}
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

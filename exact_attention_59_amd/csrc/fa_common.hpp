@@ -26,6 +26,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr float kLn2 = 0.693147180559945309417f;
@@ -46,6 +48,18 @@ __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, kWave)); }
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, kWave); }
 
+// Combine a value across the two 32-lane halves of the wave (v_permlane32_swap:
+// lanes 32..63 of one copy trade places with lanes 0..31 of the other).
+__device__ __forceinline__ float half_swap_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum of the two halves' values, added in the same order in every lane.
+__device__ __forceinline__ float half_swap_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Round two floats to bf16 (RNE, v_cvt_pk_bf16_f32) and pack them, lo first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2 r;
@@ -55,6 +69,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ds_read_b64_tr_b16 (gfx950): in each group of 16 lanes, lane i supplies the address of
+// 4 consecutive 16-bit elements (row i/4 of a 4-row block, columns 4*(i%4)..+3) and
+// receives element i of every row: result[e] = row e, column i.  `p` must point into LDS.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
 
 // bf16 (raw bits) -> float, exact.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

@@ -8,15 +8,20 @@
 // Work decomposition (FA2 order, split-Q):
 //   - one workgroup of 4 waves per (batch, head, 128-row query tile); each wave owns
 //     32 query rows, so no cross-wave reduction is ever needed;
-//   - the workgroup walks the 64-key tiles K_j, V_j once; both are staged in LDS
-//     (K row-major, V transposed) and shared by the 4 waves;
+//   - the workgroup walks the 64-key tiles K_j, V_j once; both are staged row-major
+//     in LDS (bank-conflict-free strides), double-buffered, and shared by the 4 waves;
+//     one barrier per tile;
+//   - software pipeline inside each wave: the MFMAs of tile j+1's scores are issued
+//     next to tile j's softmax (they are independent), so the matrix cores work while
+//     the vector ALUs compute exp; the rescale of acc is skipped unless the running
+//     max grows by more than a fixed slack (exact: the max cancels in acc / l);
 //   - under the causal mask the tile loop stops at the last tile any row of the
 //     workgroup can see, and a wave skips tiles its own rows cannot see; only tiles
 //     crossing the diagonal or the ragged end of K are masked element-wise;
-//   - workgroup ids are ordered tile-rank-major so that, under the causal mask, the
-//     longest query tiles start first, and workgroups sharing a K/V head land on the
-//     same XCD (consecutive ids go round-robin over the 8 XCDs and B*H is a
-//     multiple of 8 in the usual shapes).
+//   - under the causal mask a workgroup takes two query tiles, i and T_r-1-i, so every
+//     workgroup does the same work (no tail of long tiles);
+//   - workgroup ids are mapped so that the workgroups of a head share an XCD (and its
+//     L2) and are resident together.
 //
 // Register layout: the scores are computed transposed, S^T = K_j Q_i^T, with
 // v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = head dim).  A lane then holds
@@ -24,7 +29,7 @@
 // lane-local plus a single exchange between the two 32-lane halves.  The fp32 P^T
 // values, rounded to bf16, are already in the layout of the B operand of the second
 // product O^T += V_j^T P^T; the key order inside that contraction is permuted to
-// match, and V_j^T is read from LDS in the same order.  O^T keeps one query row per
+// match, and V_j^T is read from row-major LDS with gfx950's transposing LDS read.  O^T keeps one query row per
 // lane, so the rescale by alpha is a per-lane scalar multiply.
 //
 // Softmax in base 2: t = s * scale * log2(e); m is kept in t units;
@@ -41,15 +46,43 @@ struct FwdCfg {
     static constexpr int BR = kFwdBlockRows;  // query rows per workgroup
     static constexpr int BC = kFwdBlockCols;  // keys per tile
     static constexpr int THREADS = 256;
-    static constexpr int KS = D + 8;   // LDS row stride (elements) of the K tile [BC][D]
-    static constexpr int VS = BC + 8;  // LDS row stride (elements) of the V^T tile [D][BC]
+    // LDS row strides (elements).  K [BC][D]: 16 consecutive rows read 16 bytes each at one
+    // column must hit distinct banks, so rows are D + 8 apart (4 dwords mod 64 banks).
+    // V [BC][D]: the transposing reads take 4 rows x 32 d-values per 32 lanes, so rows are
+    // D + 32 apart (16 dwords mod 64 banks).
+    static constexpr int KS = D + 8;
+    static constexpr int VS = D + 32;
     static constexpr int CHUNKS_PER_ROW = D / 8;                    // 16-byte chunks per K/V row
-    static constexpr int K_CHUNKS = BC * CHUNKS_PER_ROW / THREADS;  // K chunks per thread
-    static constexpr int V_KPT = BC * CHUNKS_PER_ROW / THREADS;     // V keys per thread (one chunk each)
-    static constexpr int LDS_ELEMS = BC * KS + D * VS;
-    static_assert(K_CHUNKS >= 1 && V_KPT >= 2 && V_KPT % 2 == 0, "tile too small for the thread count");
-    static_assert(THREADS / CHUNKS_PER_ROW * V_KPT == BC, "V transpose mapping must cover the tile");
+    static constexpr int CHUNKS = BC * CHUNKS_PER_ROW / THREADS;    // chunks per thread per tile
+    static constexpr int K_TILE = BC * KS;                          // elements per K buffer
+    static constexpr int V_TILE = BC * VS;                          // elements per V buffer
+    static constexpr int V_OFF = 2 * K_TILE;
+    static constexpr int LDS_ELEMS = 2 * K_TILE + 2 * V_TILE;       // K and V, double-buffered
+    static_assert(CHUNKS >= 1 && CHUNKS * THREADS == BC * CHUNKS_PER_ROW, "tile/thread mismatch");
 };
+
+// Lazy rescale threshold (log2 units).  The running max m is only moved when a tile's
+// max exceeds it by more than this; until then p = 2^(t - m) <= 2^kRescaleSlack, which
+// fp32 and bf16 hold exactly as well as p <= 1.  The result is the same exact softmax:
+// whatever m is used, it cancels between the numerator acc and the denominator l.
+constexpr float kRescaleSlack = 8.0f;
+
+// Workgroup id -> (b*H + h, rank).  Consecutive ids are dispatched round-robin over the 8
+// XCDs, each with its own L2.  When B*H is a multiple of 8, every workgroup of a head goes
+// to the same XCD (id % 8 == head % 8) and, within an XCD, ids walk head by head, so the
+// workgroups of a head are resident together and each K/V tile is fetched into L2 once
+// and shared.  Otherwise ids go rank-major over all heads.
+__device__ __forceinline__ void map_block(int bid, int n_ranks, int BH, int& bh, int& rank) {
+    if ((BH & 7) == 0) {
+        const int xcd = bid & 7, li = bid >> 3;
+        const int hl = li / n_ranks;
+        rank = li - hl * n_ranks;
+        bh = xcd + 8 * hl;
+    } else {
+        rank = bid / BH;
+        bh = bid - rank * BH;
+    }
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
@@ -61,17 +94,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     using C = FwdCfg<D>;
     constexpr int BR = C::BR, BC = C::BC, KS = C::KS, VS = C::VS, CPR = C::CHUNKS_PER_ROW;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-    uint16_t* Ks = smem;
-    uint16_t* Vt = smem + BC * KS;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
 
-    const int bid = blockIdx.x;
-    const int rank = bid / BH;
-    const int bh = bid - rank * BH;
-    const int q_tile = CAUSAL ? (T_r - 1 - rank) : rank;
+    // Causal rows get longer with the query index, so a causal workgroup takes the pair of
+    // query tiles (T_r-1-rank, rank): every workgroup then carries the same work.
+    const int n_ranks = CAUSAL ? (T_r + 1) / 2 : T_r;
+    int bh, rank;
+    map_block(blockIdx.x, n_ranks, BH, bh, rank);
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / H_kv);
     const int64_t q_base = (int64_t)bh * N_q * D;
@@ -79,10 +111,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     const int off = N_k - N_q;  // bottom-right causal alignment
     const int T_c = (N_k + BC - 1) / BC;
 
+  auto run_tile = [&](const int q_tile) {
     const int q0w = q_tile * BR + w * 32;  // first query row of this wave
     const int q_row = q0w + l32;           // this lane's query row
 
-    // Tiles the workgroup walks and tiles this wave computes.
+    // Tiles the workgroup walks (n_tiles) and tiles this wave computes (n_w <= n_tiles).
     int n_tiles = T_c, n_w = T_c;
     {
         const int last_row = min(q_tile * BR + BR, N_q) - 1;
@@ -106,80 +139,76 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
         for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
 
-    // Global -> register staging of one K/V tile (rows past N_k read as zero).
-    u32x4 kreg[C::K_CHUNKS], vreg[C::V_KPT];
-    const int v_dc = tid % CPR, v_kg = tid / CPR;
-    auto load_tile = [&](int j) {
+    // ---- global -> register staging (rows past N_k read as zero) and register -> LDS.
+    // Thread t moves 16-byte chunks t, t + 256, ... of the tile (row-major, coalesced).
+    u32x4 kst[C::CHUNKS], vst[C::CHUNKS];
+    auto load_rows = [&](const uint16_t* __restrict__ src, int j, u32x4 (&dst)[C::CHUNKS]) {
         const int key0 = j * BC;
 #pragma unroll
-        for (int r = 0; r < C::K_CHUNKS; ++r) {
+        for (int r = 0; r < C::CHUNKS; ++r) {
             const int cidx = tid + C::THREADS * r;
             const int key = key0 + cidx / CPR, dc = cidx % CPR;
             const int key_c = min(key, N_k - 1);  // in-bounds address; the value is zeroed below
-            kreg[r] = key < N_k ? *reinterpret_cast<const u32x4*>(K + kv_base + (int64_t)key_c * D + dc * 8)
-                                : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int r = 0; r < C::V_KPT; ++r) {
-            const int key = key0 + v_kg * C::V_KPT + r;
-            const int key_c = min(key, N_k - 1);
-            vreg[r] = key < N_k ? *reinterpret_cast<const u32x4*>(V + kv_base + (int64_t)key_c * D + v_dc * 8)
-                                : u32x4{0, 0, 0, 0};
+            dst[r] = key < N_k ? *reinterpret_cast<const u32x4*>(src + kv_base + (int64_t)key_c * D + dc * 8)
+                               : u32x4{0, 0, 0, 0};
         }
     };
-    // Register -> LDS: K row-major; V transposed to Vt[d][key] (pairs of keys per 32-bit word).
-    auto store_tile = [&]() {
+    auto load_k = [&](int j) { load_rows(K, j, kst); };
+    auto load_v = [&](int j) { load_rows(V, j, vst); };
+    auto store_rows = [&](uint16_t* base, int stride, const u32x4 (&src)[C::CHUNKS]) {
 #pragma unroll
-        for (int r = 0; r < C::K_CHUNKS; ++r) {
+        for (int r = 0; r < C::CHUNKS; ++r) {
             const int cidx = tid + C::THREADS * r;
-            *reinterpret_cast<u32x4*>(Ks + (cidx / CPR) * KS + (cidx % CPR) * 8) = kreg[r];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t words[C::V_KPT / 2];
-#pragma unroll
-            for (int p = 0; p < C::V_KPT / 2; ++p) {
-                const uint32_t a = vreg[2 * p][e >> 1], bb = vreg[2 * p + 1][e >> 1];
-                words[p] = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-            }
-            uint16_t* dst = Vt + (v_dc * 8 + e) * VS + v_kg * C::V_KPT;
-            if constexpr (C::V_KPT == 4) {
-                *reinterpret_cast<u32x2*>(dst) = u32x2{words[0], words[1]};
-            } else if constexpr (C::V_KPT == 2) {
-                *reinterpret_cast<uint32_t*>(dst) = words[0];
-            } else {
-#pragma unroll
-                for (int p = 0; p < C::V_KPT / 2; ++p) reinterpret_cast<uint32_t*>(dst)[p] = words[p];
-            }
+            *reinterpret_cast<u32x4*>(base + (cidx / CPR) * stride + (cidx % CPR) * 8) = src[r];
         }
     };
+    auto store_k = [&](int buf) { store_rows(smem + buf * C::K_TILE, KS, kst); };
+    auto store_v = [&](int buf) { store_rows(smem + C::V_OFF + buf * C::V_TILE, VS, vst); };
 
-    float m2 = -INFINITY;  // running max, in units of log2(e) * scale * score
-    float lsum = 0.f;      // running sum of 2^(t - m2)
+    // ---- the two contractions
+    // S^T[key][query] = K_j Q^T for the two 32-key blocks of the tile (chains interleaved).
+    auto qk = [&](int buf, f32x16 (&s)[BC / 32]) {
+        const uint16_t* Ks = smem + buf * C::K_TILE;
+#pragma unroll
+        for (int mb = 0; mb < BC / 32; ++mb) s[mb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < BC / 32; ++mb)
+                s[mb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + (32 * mb + l32) * KS + 8 * hh + 16 * ks),
+                               qf[ks], s[mb]);
+    };
+    // O^T[d][query] += V_j^T P^T.  P^T is the B operand: for 16-key step k2, half hh of
+    // the wave holds keys 16*k2 + 4*hh + (0..3) and 16*k2 + 8 + 4*hh + (0..3).  The A
+    // operand V_j^T comes from row-major V in LDS through ds_read_b64_tr_b16: in each
+    // 16-lane group, lane i addresses row i/4, columns 4*(i%4)..+3 of a 4-key x 16-d
+    // block and receives column i (4 consecutive keys at one d).  Groups 0/1 (2/3) cover
+    // d = 32*db + 0..15 / 16..31 for half 0 (1); two reads give the 8 keys of the slot.
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-
-    if (n_tiles > 0) load_tile(0);
-    for (int j = 0; j < n_tiles; ++j) {
-        __syncthreads();  // every wave is done with tile j-1
-        store_tile();
-        __syncthreads();  // tile j visible to every wave
-        if (j + 1 < n_tiles) load_tile(j + 1);
-        if (j >= n_w) continue;
-
-        // S^T[key][query] = K_j Q^T   (two 32-key blocks)
-        f32x16 s[BC / 32];
+    const int tr_off = (4 * hh + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto pv = [&](int buf, const bf16x8 (&pf)[BC / 16]) {
+        const uint16_t* Vs = smem + C::V_OFF + buf * C::V_TILE + tr_off;
 #pragma unroll
-        for (int mb = 0; mb < BC / 32; ++mb) {
-            s[mb] = f32x16{};
-            const uint16_t* kp = Ks + (32 * mb + l32) * KS + 8 * hh;
+        for (int k2 = 0; k2 < BC / 16; ++k2)
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                s[mb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + 16 * ks), qf[ks], s[mb]);
-        }
+            for (int db = 0; db < D / 32; ++db) {
+                const uint16_t* p = Vs + 16 * k2 * VS + 32 * db;
+                const i16x4 lo = lds_read_tr16(p);
+                const i16x4 hi = lds_read_tr16(p + 8 * VS);
+                acc[db] = mfma32(__builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}),
+                                 pf[k2], acc[db]);
+            }
+    };
 
-        // Element mask on ragged or diagonal tiles only.
+    // ---- online softmax state of this lane's query row (both 32-lane halves hold it)
+    float m2 = -INFINITY;  // running (possibly stale) max, in units of log2(e) * scale * score
+    float lsum = 0.f;      // this half's share of sum 2^(t - m2); the halves are added at the end
+
+    // Mask (ragged or diagonal tiles only), row max, and the rare rescale.  Returns the
+    // max to subtract in the exponent.
+    auto softmax_prepare = [&](f32x16 (&s)[BC / 32], int j) -> float {
         const int key0 = j * BC;
         const bool ragged = key0 + BC > N_k;
         const bool diag = CAUSAL && (key0 + BC - 1 > q0w + off);
@@ -193,17 +222,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
                     if (key > lim) s[mb][r] = -INFINITY;
                 }
         }
-
-        // Online softmax update (row = this lane's query; the other half holds the other keys).
         float mx = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < BC / 32; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-        mx = xor_max(mx, 32);
-        const float m_new = fmaxf(m2, mx * c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2_hw(m2 - m_use);
+        mx = half_swap_max(mx);
+        const float t_max = mx * c;
+        const bool need = t_max > m2 + kRescaleSlack;  // false for -inf rows
+        if (__any(need)) {
+            // Lanes that keep their max use alpha = 1 (their m may still be -inf, and
+            // -inf - -inf must not reach exp2); a first max gives alpha = 2^-inf = 0.
+            const float alpha = need ? exp2_hw(m2 - t_max) : 1.f;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+            m2 = need ? t_max : m2;
+        }
+        return m2 == -INFINITY ? 0.f : m2;
+    };
+    // p = 2^(s*c - m), lane-local partial sum, P^T packed to bf16 as the B operand.
+    auto softmax_finish = [&](f32x16 (&s)[BC / 32], float m_use, bf16x8 (&pf)[BC / 16]) {
         float ps = 0.f;
 #pragma unroll
         for (int mb = 0; mb < BC / 32; ++mb)
@@ -213,15 +252,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
                 s[mb][r] = p;
                 ps += p;
             }
-        ps = xor_sum(ps, 32);
-        lsum = fmaf(lsum, alpha, ps);
-        m2 = m_new;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-
-        // P^T as B operand: 16-key step k2 uses registers 8*(k2&1) .. +7 of block k2/2,
-        // i.e. keys 16*k2 + 8*(e/4) + 4*hh + e%4 for e = 0..7.
-        bf16x8 pf[BC / 16];
+        lsum += ps;
 #pragma unroll
         for (int k2 = 0; k2 < BC / 16; ++k2) {
             const int mb = k2 >> 1, r0 = 8 * (k2 & 1);
@@ -230,20 +261,53 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
                                      pack_bf16x2(s[mb][r0 + 4], s[mb][r0 + 5]),
                                      pack_bf16x2(s[mb][r0 + 6], s[mb][r0 + 7])});
         }
+    };
 
-        // O^T[d][query] += V_j^T P^T, V^T read in the same permuted key order.
-#pragma unroll
-        for (int k2 = 0; k2 < BC / 16; ++k2)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint16_t* vp = Vt + (32 * db + l32) * VS + 16 * k2 + 4 * hh;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-                acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[k2], acc[db]);
-            }
+    // ---- pipeline: tile j+1's QK is issued while tile j's softmax runs.
+    // LDS: K buffers hold K_{j+1} (read now) and K_{j+2} (being written); V buffers hold
+    // V_j (read now) and V_{j+1} (being written).  One barrier per tile.
+    f32x16 sA[BC / 32], sB[BC / 32];
+    if (n_tiles > 0) {
+        load_k(0);
+        load_v(0);
+        store_k(0);
+        store_v(0);
+        if (n_tiles > 1) {
+            load_k(1);
+            store_k(1);
+            load_v(1);
+        }
+        if (n_tiles > 2) load_k(2);
+        __syncthreads();
+        if (n_w > 0) qk(0, sA);
+        __syncthreads();
+    }
+
+    auto step = [&](int j, f32x16 (&s_cur)[BC / 32], f32x16 (&s_next)[BC / 32]) {
+        // stage the next tiles: K_{j+2} -> K buffer j%2, V_{j+1} -> V buffer (j+1)%2
+        if (j + 2 < n_tiles) store_k(j & 1);
+        if (j + 1 < n_tiles) store_v((j + 1) & 1);
+        if (j + 3 < n_tiles) load_k(j + 3);
+        if (j + 2 < n_tiles) load_v(j + 2);
+        if (j < n_w) {
+            const float m_use = softmax_prepare(s_cur, j);
+            bf16x8 pf[BC / 16];
+            // Tile j+1's scores, issued unconditionally so that the MFMAs share a basic
+            // block with the exps below and overlap them.  Past this wave's last tile the
+            // buffer holds other (finite or stale) data and the result is never used.
+            qk((j + 1) & 1, s_next);
+            softmax_finish(s_cur, m_use, pf);
+            pv(j & 1, pf);
+        }
+        __syncthreads();
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+        step(j, sA, sB);
+        if (j + 1 < n_tiles) step(j + 1, sB, sA);
     }
 
     // Epilogue: O = acc / l (once), LSE = (m + log2 l) ln 2.
+    lsum = half_swap_sum(lsum);
     if (q_row < N_q) {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         uint16_t* op = O + q_base + (int64_t)q_row * D;
@@ -258,6 +322,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
             }
         if (hh == 0) LSE[(int64_t)bh * N_q + q_row] = lsum > 0.f ? (m2 + log2_hw(lsum)) * kLn2 : -INFINITY;
     }
+  };
+
+    run_tile(CAUSAL ? T_r - 1 - rank : rank);
+    if (CAUSAL && rank != T_r - 1 - rank) {
+        __syncthreads();  // the first tile's last LDS reads are done before the next prologue
+        run_tile(rank);
+    }
 }
 
 template <int D, bool CAUSAL>
@@ -266,7 +337,7 @@ hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, fl
     const int T_r = (N_q + kFwdBlockRows - 1) / kFwdBlockRows;
     const int BH = B * H;
     const float c = (float)((double)scale * 1.4426950408889634073599);
-    const long long blocks = (long long)T_r * BH;
+    const long long blocks = (long long)(CAUSAL ? (T_r + 1) / 2 : T_r) * BH;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                        static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), LSE, H, H_kv, N_q, N_k,
