@@ -70,6 +70,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Copy a value through an opaque v_mov, once, outside a loop.  The copy is produced by a
+// VALU instruction, so the compiler's wait-count bookkeeping no longer ties it to the
+// global load that filled the source registers (otherwise the loop may wait on in-flight
+// prefetch loads before every use of the value).
+__device__ __forceinline__ u32x4 vgpr_copy(u32x4 v) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("v_mov_b32 %0, %1" : "=v"(r[i]) : "v"(v[i]));
+    return r;
+}
+
 // ds_read_b64_tr_b16 (gfx950): in each group of 16 lanes, lane i supplies the address of
 // 4 consecutive 16-bit elements (row i/4 of a 4-row block, columns 4*(i%4)..+3) and
 // receives element i of every row: result[e] = row e, column i.  `p` must point into LDS.

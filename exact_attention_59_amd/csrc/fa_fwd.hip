@@ -35,6 +35,8 @@
 // Softmax in base 2: t = s * scale * log2(e); m is kept in t units;
 // p = 2^(t - m), alpha = 2^(m_old - m_new); LSE = (m + log2 l) * ln 2.
 // l sums the fp32 p (before rounding P to bf16).
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -46,20 +48,25 @@ struct FwdCfg {
     static constexpr int BR = kFwdBlockRows;  // query rows per workgroup
     static constexpr int BC = kFwdBlockCols;  // keys per tile
     static constexpr int THREADS = 256;
-    // LDS row strides (elements).  K [BC][D]: 16 consecutive rows read 16 bytes each at one
-    // column must hit distinct banks, so rows are D + 8 apart (4 dwords mod 64 banks).
-    // V [BC][D]: the transposing reads take 4 rows x 32 d-values per 32 lanes, so rows are
-    // D + 32 apart (16 dwords mod 64 banks).
-    static constexpr int KS = D + 8;
-    static constexpr int VS = D + 32;
-    static constexpr int CHUNKS_PER_ROW = D / 8;                    // 16-byte chunks per K/V row
-    static constexpr int CHUNKS = BC * CHUNKS_PER_ROW / THREADS;    // chunks per thread per tile
-    static constexpr int K_TILE = BC * KS;                          // elements per K buffer
-    static constexpr int V_TILE = BC * VS;                          // elements per V buffer
-    static constexpr int V_OFF = 2 * K_TILE;
-    static constexpr int LDS_ELEMS = 2 * K_TILE + 2 * V_TILE;       // K and V, double-buffered
-    static_assert(CHUNKS >= 1 && CHUNKS * THREADS == BC * CHUNKS_PER_ROW, "tile/thread mismatch");
+    static constexpr int TILE = BC * D;       // elements of one K or V tile buffer (rows unpadded)
+    // A 64-lane global->LDS copy moves 1 KB; the 4 waves split a tile's copies evenly.
+    static constexpr int DMA_PER_WAVE = BC * D * 2 / 1024 / 4;
+    static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * 4 * 1024 == BC * D * 2, "tile must split into 1 KB copies");
 };
+
+// LDS tiles are row-major without padding; the 16-byte chunks of row r are stored at
+// chunk index c ^ swz(r) so that both read patterns are bank-conflict-free (64 banks):
+//   K (QK A operand): 16 consecutive rows, one chunk each -> 16 distinct chunk slots;
+//   V (transposing reads): 4 consecutive rows x 4 consecutive chunks (32 d-values) -> 16
+//   distinct slots.  A row of d = 128 spans all 64 banks, a row of d = 64 half of them.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained): this wave's global->LDS
+// copies have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Lazy rescale threshold (log2 units).  The running max m is only moved when a tile's
 // max exceeds it by more than this; until then p = 2^(t - m) <= 2^kRescaleSlack, which
@@ -92,8 +99,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
                                                      int H, int H_kv, int N_q, int N_k, int T_r, int BH,
                                                      float c) {
     using C = FwdCfg<D>;
-    constexpr int BR = C::BR, BC = C::BC, KS = C::KS, VS = C::VS, CPR = C::CHUNKS_PER_ROW;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+    constexpr int BR = C::BR, BC = C::BC;
+    // Separate arrays per buffer, so that copies into one buffer and reads of another are
+    // known not to overlap.
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[C::TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -133,50 +145,51 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     if (q_row < N_q) {
         const u32x4* qp = reinterpret_cast<const u32x4*>(Q + q_base + (int64_t)q_row * D + 8 * hh);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(qp[2 * ks]);
+        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(vgpr_copy(qp[2 * ks]));
     } else {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
 
-    // ---- global -> register staging (rows past N_k read as zero) and register -> LDS.
-    // Thread t moves 16-byte chunks t, t + 256, ... of the tile (row-major, coalesced).
-    u32x4 kst[C::CHUNKS], vst[C::CHUNKS];
-    auto load_rows = [&](const uint16_t* __restrict__ src, int j, u32x4 (&dst)[C::CHUNKS]) {
+    // ---- global -> LDS copies (no registers involved).  Copy t of this wave fills LDS
+    // block (w * DMA_PER_WAVE + t), 1 KB; lane l's 16 bytes land at offset 16*l in it,
+    // i.e. at row r, stored chunk sc; the lane reads logical chunk sc ^ swz(r) of row r.
+    // Rows past N_k repeat row N_k - 1 (finite data whose scores are masked, P = 0).
+    constexpr int ROWS_PER_COPY = 512 / D;
+    const int dma_r0 = w * C::DMA_PER_WAVE * ROWS_PER_COPY + lane / (D / 8);
+    const int dma_sc = lane % (D / 8);
+    auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* dst, bool is_v) {
         const int key0 = j * BC;
+        const uint16_t* head = src + kv_base;
 #pragma unroll
-        for (int r = 0; r < C::CHUNKS; ++r) {
-            const int cidx = tid + C::THREADS * r;
-            const int key = key0 + cidx / CPR, dc = cidx % CPR;
-            const int key_c = min(key, N_k - 1);  // in-bounds address; the value is zeroed below
-            dst[r] = key < N_k ? *reinterpret_cast<const u32x4*>(src + kv_base + (int64_t)key_c * D + dc * 8)
-                               : u32x4{0, 0, 0, 0};
+        for (int t = 0; t < C::DMA_PER_WAVE; ++t) {
+            const int r = dma_r0 + t * ROWS_PER_COPY;
+            const int c = dma_sc ^ (is_v ? swz_v<D>(r) : swz_k<D>(r));
+            const uint16_t* g = head + (int64_t)min(key0 + r, N_k - 1) * D + 8 * c;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(g),
+                (__attribute__((address_space(3))) void*)(dst + (w * C::DMA_PER_WAVE + t) * 512), 16, 0, 0);
         }
     };
-    auto load_k = [&](int j) { load_rows(K, j, kst); };
-    auto load_v = [&](int j) { load_rows(V, j, vst); };
-    auto store_rows = [&](uint16_t* base, int stride, const u32x4 (&src)[C::CHUNKS]) {
-#pragma unroll
-        for (int r = 0; r < C::CHUNKS; ++r) {
-            const int cidx = tid + C::THREADS * r;
-            *reinterpret_cast<u32x4*>(base + (cidx / CPR) * stride + (cidx % CPR) * 8) = src[r];
-        }
-    };
-    auto store_k = [&](int buf) { store_rows(smem + buf * C::K_TILE, KS, kst); };
-    auto store_v = [&](int buf) { store_rows(smem + C::V_OFF + buf * C::V_TILE, VS, vst); };
 
     // ---- the two contractions
     // S^T[key][query] = K_j Q^T for the two 32-key blocks of the tile (chains interleaved).
-    auto qk = [&](int buf, f32x16 (&s)[BC / 32]) {
-        const uint16_t* Ks = smem + buf * C::K_TILE;
+    // Lane reads row 32*mb + l32, logical chunk 2*ks + hh; the swizzle of that row depends
+    // on l32 only, so the per-ks offsets are fixed per lane.
+    int k_off[D / 16];
+    {
+        const int sk = swz_k<D>(l32);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = l32 * D + 8 * ((2 * ks + hh) ^ sk);
+    }
+    auto qk = [&](const uint16_t* Ks, f32x16 (&s)[BC / 32]) {
 #pragma unroll
         for (int mb = 0; mb < BC / 32; ++mb) s[mb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
             for (int mb = 0; mb < BC / 32; ++mb)
-                s[mb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + (32 * mb + l32) * KS + 8 * hh + 16 * ks),
-                               qf[ks], s[mb]);
+                s[mb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + k_off[ks] + 32 * mb * D), qf[ks], s[mb]);
     };
     // O^T[d][query] += V_j^T P^T.  P^T is the B operand: for 16-key step k2, half hh of
     // the wave holds keys 16*k2 + 4*hh + (0..3) and 16*k2 + 8 + 4*hh + (0..3).  The A
@@ -187,16 +200,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-    const int tr_off = (4 * hh + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    auto pv = [&](int buf, const bf16x8 (&pf)[BC / 16]) {
-        const uint16_t* Vs = smem + C::V_OFF + buf * C::V_TILE + tr_off;
+    // With the swizzle, lane (i = lane % 16) reads row 16*k2 + 8*x + 4*hh + i/4, stored
+    // chunk (4*db + cg) ^ swz_v(row) where cg = 2*((lane/16)%2) + (i%4)/2, plus 4*(i%2)
+    // elements; swz_v of those rows depends on i only.
+    int v_off[D / 32];
+    {
+        const int i = lane & 15;
+        const int sv = swz_v<D>(4 * hh + (i >> 2)) >> 2;
+        const int cg = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            v_off[db] = (4 * hh + (i >> 2)) * D + 32 * (db ^ sv) + 8 * cg + 4 * (i & 1);
+    }
+    auto pv = [&](const uint16_t* Vs, const bf16x8 (&pf)[BC / 16]) {
 #pragma unroll
         for (int k2 = 0; k2 < BC / 16; ++k2)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const uint16_t* p = Vs + 16 * k2 * VS + 32 * db;
+                const uint16_t* p = Vs + v_off[db] + 16 * k2 * D;
                 const i16x4 lo = lds_read_tr16(p);
-                const i16x4 hi = lds_read_tr16(p + 8 * VS);
+                const i16x4 hi = lds_read_tr16(p + 8 * D);
                 acc[db] = mfma32(__builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}),
                                  pf[k2], acc[db]);
             }
@@ -264,46 +287,45 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     };
 
     // ---- pipeline: tile j+1's QK is issued while tile j's softmax runs.
-    // LDS: K buffers hold K_{j+1} (read now) and K_{j+2} (being written); V buffers hold
-    // V_j (read now) and V_{j+1} (being written).  One barrier per tile.
+    // LDS: K buffers hold K_{j+1} (read now) and K_{j+2} (being copied in); V buffers hold
+    // V_j (read now) and V_{j+1} (being copied in).  One barrier per tile.  The loop is
+    // unrolled by two so that every buffer choice is a compile-time constant.
     f32x16 sA[BC / 32], sB[BC / 32];
     if (n_tiles > 0) {
-        load_k(0);
-        load_v(0);
-        store_k(0);
-        store_v(0);
-        if (n_tiles > 1) {
-            load_k(1);
-            store_k(1);
-            load_v(1);
-        }
-        if (n_tiles > 2) load_k(2);
+        dma_tile(K, 0, k_lds0, false);
+        dma_tile(V, 0, v_lds0, true);
+        if (n_tiles > 1) dma_tile(K, 1, k_lds1, false);
+        wait_vmem();
         __syncthreads();
-        if (n_w > 0) qk(0, sA);
+        // Unconditional (a wave with no rows to compute ignores the result).
+        qk(k_lds0, sA);
         __syncthreads();
     }
 
-    auto step = [&](int j, f32x16 (&s_cur)[BC / 32], f32x16 (&s_next)[BC / 32]) {
-        // stage the next tiles: K_{j+2} -> K buffer j%2, V_{j+1} -> V buffer (j+1)%2
-        if (j + 2 < n_tiles) store_k(j & 1);
-        if (j + 1 < n_tiles) store_v((j + 1) & 1);
-        if (j + 3 < n_tiles) load_k(j + 3);
-        if (j + 2 < n_tiles) load_v(j + 2);
+    auto step = [&](auto parity, int j, f32x16 (&s_cur)[BC / 32], f32x16 (&s_next)[BC / 32]) {
+        constexpr bool odd = decltype(parity)::value;
+        uint16_t* const k_fill = odd ? k_lds1 : k_lds0;  // receives K_{j+2}
+        uint16_t* const k_read = odd ? k_lds0 : k_lds1;  // holds K_{j+1}
+        uint16_t* const v_fill = odd ? v_lds0 : v_lds1;  // receives V_{j+1}
+        uint16_t* const v_read = odd ? v_lds1 : v_lds0;  // holds V_j
+        if (j + 2 < n_tiles) dma_tile(K, j + 2, k_fill, false);
+        if (j + 1 < n_tiles) dma_tile(V, j + 1, v_fill, true);
         if (j < n_w) {
             const float m_use = softmax_prepare(s_cur, j);
             bf16x8 pf[BC / 16];
             // Tile j+1's scores, issued unconditionally so that the MFMAs share a basic
             // block with the exps below and overlap them.  Past this wave's last tile the
-            // buffer holds other (finite or stale) data and the result is never used.
-            qk((j + 1) & 1, s_next);
+            // buffer holds other finite data and the result is never used.
+            qk(k_read, s_next);
             softmax_finish(s_cur, m_use, pf);
-            pv(j & 1, pf);
+            pv(v_read, pf);
         }
+        wait_vmem();
         __syncthreads();
     };
     for (int j = 0; j < n_tiles; j += 2) {
-        step(j, sA, sB);
-        if (j + 1 < n_tiles) step(j + 1, sB, sA);
+        step(std::integral_constant<bool, false>{}, j, sA, sB);
+        if (j + 1 < n_tiles) step(std::integral_constant<bool, true>{}, j + 1, sB, sA);
     }
 
     // Epilogue: O = acc / l (once), LSE = (m + log2 l) ln 2.
