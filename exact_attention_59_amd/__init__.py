@@ -73,15 +73,22 @@ def _check(fn: str, status: int):
         raise FAError(fn, status)
 
 
-def _torch():
-    import torch
+_torch_mod = None
 
-    return torch
+
+def _torch():
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _stream_ptr(t):
+    """Raw hipStream_t of torch's current stream on t's device (no Stream object built)."""
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return torch._C._cuda_getCurrentRawStream(t.device.index)
 
 
 def _need(t, name, dtype, ndim):

@@ -91,8 +91,13 @@ __device__ __forceinline__ void map_block(int bid, int n_ranks, int BH, int& bh,
     }
 }
 
+// Two workgroups (8 waves) per CU.  (Three fit at d = 64 but measured no faster: the
+// loop is bound by LDS read throughput, not by latency.)
+template <int D>
+constexpr int kFwdBlocksPerCU = 2;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ O, float* __restrict__ LSE,
