@@ -8,8 +8,8 @@ bf16), once without and once with the causal mask.  `value` is that step's nomin
 FLOPs (4*B*H*N_q*N_k*d, halved under the causal mask) over its GPU time, in TFLOPS.
 The flash-decoding leg (B=4, H=32, H_kv=8, d=128, N_k = 4096 and 65536; split kernel
 then combine kernel) runs in the same invocation and is reported under "decode" in
-GB/s of K+V read once, against the 8 TB/s HBM peak; the 256 MB last-level cache is
-overwritten before every timed decode repetition so K/V come from HBM.
+GB/s of K+V read once, against the 8 TB/s HBM peak; a 640 MB read sweep before every
+timed decode repetition evicts K/V from the 256 MB last-level cache.
 
 Inputs are synthetic and seeded (counter-based SplitMix64 + Box-Muller, see gen/),
 already resident in device memory when timing starts.  GPU times come from HIP
@@ -159,15 +159,17 @@ def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=
     o = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     kv_bytes = 2.0 * B * H_kv * N_k * d * 2
-    # Overwrite the last-level cache (256 MB) before every timed repetition.
-    flush = torch.empty(640 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    # Before every timed repetition, sweep-read 640 MB so the 256 MB last-level cache holds
+    # other (clean) lines and K/V come from HBM.  A read sweep, not a write: dirty lines
+    # would be written back during the decode kernel and steal its bandwidth.
+    flush = torch.ones(640 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     for _ in range(3):
         fa.decode_split(q, k, v, S, o_part=o_part, lse_part=l_part)
         fa.combine(o_part, l_part, out=o, lse=lse)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
     for i in range(reps):
-        flush.fill_(float(i))
+        torch.amax(flush)
         evs[i][0].record(stream)
         fa.decode_split(q, k, v, S, o_part=o_part, lse_part=l_part)
         evs[i][1].record(stream)

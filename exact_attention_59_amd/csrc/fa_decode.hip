@@ -13,14 +13,13 @@
 //   - the 4 waves of a workgroup take interleaved 32-key blocks of the segment and
 //     keep independent online states; they are merged once at the end through LDS.
 //     Waves never wait for each other inside the key loop;
-//   - each wave loads its next block into registers while it computes the current
-//     one (about 16 KB in flight per wave at d = 128);
+//   - each wave keeps two blocks in flight beyond the one it computes (a two-slot
+//     register ring, refilled as soon as a slot's data is consumed);
 //   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane holds one query (lane % 16)
-//     and 8 of every 32 keys; K comes straight from global memory in A-operand layout
-//     (each lane reads 64 contiguous bytes of one key row per 16-key block; the head
-//     dimension is permuted inside the contraction to make that possible);
-//   - O^T += V^T P^T needs V transposed: each wave writes its V block to its own LDS
-//     region as Vt[d][key] and reads it back in the permuted key order of P^T.
+//     and 8 of every 32 keys; K goes straight from global memory into A-operand
+//     registers, each load instruction reading whole 64-byte lines of 16 key rows;
+//   - O^T += V^T P^T: V is written row-major (XOR-swizzled chunks) to the wave's own
+//     LDS block and read back with the transposing LDS read in the key order of P^T.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -29,20 +28,25 @@ namespace {
 
 template <int D>
 struct DecCfg {
-    static constexpr int KB = kDecKeysPerWave;    // keys per wave iteration
+    static constexpr int KB = kDecKeysPerWave;    // keys per block
     static constexpr int NQ = kDecHeadsPerBlock;  // query heads per workgroup (MFMA N)
     static constexpr int NW = 4;
-    static constexpr int VS = KB + 8;              // LDS row stride (elements) of Vt [D][KB]
-    static constexpr int CPR = D / 8;              // 16-byte chunks per row
-    static constexpr int V_KPT = KB * CPR / 64;    // V keys per lane (one chunk each)
-    static constexpr int KSTEPS = D / 32;          // contraction steps of S^T
-    static_assert(64 / CPR * V_KPT == KB, "V transpose mapping must cover the block");
-    static_assert(V_KPT % 2 == 0, "keys per lane must pair up");
-    static constexpr int VT_ELEMS = NW * D * VS;                  // per-wave transposed V blocks
-    static constexpr int MERGE_FLOATS = NW * NQ * (D + 2);        // per-wave (m, l, acc)
+    static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int KSTEPS = D / 32;         // contraction steps of S^T (32 d each)
+    static constexpr int K_LOADS = 2 * KSTEPS;    // 16-byte K loads per lane per block
+    static constexpr int V_LOADS = KB * CPR / 64; // 16-byte V loads per lane per block
+    static constexpr int V_ELEMS = KB * D;        // one wave's LDS V block
+    static constexpr int MERGE_FLOATS = NW * NQ * (D + 2);
     static constexpr int SMEM_BYTES =
-        (VT_ELEMS * 2 > MERGE_FLOATS * 4) ? VT_ELEMS * 2 : MERGE_FLOATS * 4;
+        (NW * V_ELEMS * 2 > MERGE_FLOATS * 4) ? NW * V_ELEMS * 2 : MERGE_FLOATS * 4;
+    static_assert(V_LOADS * 64 == KB * CPR, "V block must split evenly over the lanes");
 };
+
+// Chunk swizzle of the LDS V block: the transposing reads of one pass take 8 rows x 32
+// contiguous bytes; XOR-ing the chunk index with an even per-row value keeps each 32-byte
+// pair together and puts the 8 rows on distinct banks.
+template <int D>
+__device__ __forceinline__ int dec_swz(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __restrict__ Q,
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
                                                               int H_kv, int N_k, int S, int L, int n_qc,
                                                               float c) {
     using C = DecCfg<D>;
-    constexpr int KB = C::KB, NQ = C::NQ, NW = C::NW, VS = C::VS, CPR = C::CPR;
+    constexpr int KB = C::KB, NQ = C::NQ, NW = C::NW, CPR = C::CPR;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -69,93 +73,89 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
 
     const int k_beg = min(s * L, N_k), k_end = min(k_beg + L, N_k);
     const int nblk = (k_end - k_beg + KB - 1) / KB;
-    const int64_t kv_base = (int64_t)bg * N_k * D;
+    const uint16_t* Kh = K + (int64_t)bg * N_k * D;
+    const uint16_t* Vh = V + (int64_t)bg * N_k * D;
 
     // Query head of this lane's MFMA column.
     const int qh = qc * NQ + n16;  // index inside the group
     const bool q_valid = qh < group;
     const int h = g * group + qh;
 
-    // Q fragment (B operand): lane holds Q[h][(D/4)*hq + 8*t + e] for step t (the head
-    // dimension is permuted inside the contraction so each lane reads contiguous bytes).
+    // Q fragment (B operand): lane holds Q[h][32*t + 8*hq + e] for step t.
     bf16x8 qf[C::KSTEPS];
     if (q_valid) {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(Q + ((int64_t)b * H + h) * D + (D / 4) * hq);
+        const u32x4* qp = reinterpret_cast<const u32x4*>(Q + ((int64_t)b * H + h) * D + 8 * hq);
 #pragma unroll
-        for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(qp[t]);
+        for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(vgpr_copy(qp[4 * t]));
     } else {
 #pragma unroll
         for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
 
-    uint16_t* Vt = reinterpret_cast<uint16_t*>(smem) + w * D * VS;
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem) + w * C::V_ELEMS;
 
-    // Per-wave block staging: K in A-operand layout, V as row chunks for the transpose.
-    u32x4 kreg[2][C::KSTEPS], vreg[C::V_KPT];
+    // ---- block loads.  K: lane (n16, hq) holds row 16*mb + n16, d = 32*t + 8*hq + 0..7
+    // (the 4 lanes of a row cover one 64-byte line per instruction).  V: lane holds row
+    // v_kg*V_LOADS + r, chunk v_dc.  Rows past the segment read as zero.
     const int v_dc = lane % CPR, v_kg = lane / CPR;
-    auto load_block = [&](int bi) {
+    auto load_block = [&](int bi, u32x4 (&kr)[C::K_LOADS], u32x4 (&vr)[C::V_LOADS]) {
         const int key0 = k_beg + bi * KB;
+        const bool full = key0 + KB <= k_end;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const int key = key0 + 16 * mb + n16;
-            const int key_c = min(key, N_k - 1);  // in-bounds address; the value is zeroed below
-            const u32x4* kp = reinterpret_cast<const u32x4*>(K + kv_base + (int64_t)key_c * D + (D / 4) * hq);
+            const int key_c = full ? key : min(key, N_k - 1);  // in-bounds address
+            const u32x4* kp = reinterpret_cast<const u32x4*>(Kh + (int64_t)key_c * D + 8 * hq);
 #pragma unroll
-            for (int t = 0; t < C::KSTEPS; ++t) kreg[mb][t] = key < k_end ? kp[t] : u32x4{0, 0, 0, 0};
+            for (int t = 0; t < C::KSTEPS; ++t)
+                kr[mb * C::KSTEPS + t] = (full || key < k_end) ? kp[4 * t] : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int r = 0; r < C::V_KPT; ++r) {
-            const int key = key0 + v_kg * C::V_KPT + r;
-            const int key_c = min(key, N_k - 1);
-            vreg[r] = key < k_end ? *reinterpret_cast<const u32x4*>(V + kv_base + (int64_t)key_c * D + v_dc * 8)
-                                  : u32x4{0, 0, 0, 0};
+        for (int r = 0; r < C::V_LOADS; ++r) {
+            const int key = key0 + v_kg * C::V_LOADS + r;
+            const int key_c = full ? key : min(key, N_k - 1);
+            vr[r] = (full || key < k_end) ? *reinterpret_cast<const u32x4*>(Vh + (int64_t)key_c * D + v_dc * 8)
+                                          : u32x4{0, 0, 0, 0};
         }
     };
+
+    // Transposing-read offsets for the PV A operand (V^T, M = 16 d, K = 32 keys): lane
+    // (i = n16) of group hq reads row 16*x + 4*hq + i/4, d = 16*db + 4*(i%4) .. +3.
+    int v_off[D / 16];
+    {
+        const int row = 4 * hq + (n16 >> 2);  // rows 16*x + row share the swizzle of row
+        const int sw = dec_swz<D>(row);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const int chunk = 2 * db + ((n16 & 3) >> 1);
+            v_off[db] = row * D + 8 * (chunk ^ sw) + 4 * (n16 & 1);
+        }
+    }
 
     float m2 = -INFINITY, lsum = 0.f;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
 
-    if (w < nblk) load_block(w);
-    for (int bi = w; bi < nblk; bi += NW) {
-        u32x4 kcur[2][C::KSTEPS], vcur[C::V_KPT];
+    auto compute = [&](int bi, const u32x4 (&kr)[C::K_LOADS], const u32x4 (&vr)[C::V_LOADS],
+                       auto&& refill) {
+        // V block -> this wave's LDS (row-major, swizzled chunks)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int t = 0; t < C::KSTEPS; ++t) kcur[mb][t] = kreg[mb][t];
-#pragma unroll
-        for (int r = 0; r < C::V_KPT; ++r) vcur[r] = vreg[r];
-        if (bi + NW < nblk) load_block(bi + NW);
-
-        // V block -> this wave's LDS region, transposed to Vt[d][key].
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t words[C::V_KPT / 2];
-#pragma unroll
-            for (int p = 0; p < C::V_KPT / 2; ++p) {
-                const uint32_t a = vcur[2 * p][e >> 1], bb = vcur[2 * p + 1][e >> 1];
-                words[p] = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-            }
-            uint16_t* dst = Vt + (v_dc * 8 + e) * VS + v_kg * C::V_KPT;
-            if constexpr (C::V_KPT == 8) {
-                *reinterpret_cast<u32x4*>(dst) = u32x4{words[0], words[1], words[2], words[3]};
-            } else {
-                static_assert(C::V_KPT == 4, "unsupported V keys per lane");
-                *reinterpret_cast<u32x2*>(dst) = u32x2{words[0], words[1]};
-            }
+        for (int r = 0; r < C::V_LOADS; ++r) {
+            const int row = v_kg * C::V_LOADS + r;
+            *reinterpret_cast<u32x4*>(Vs + row * D + 8 * (v_dc ^ dec_swz<D>(row))) = vr[r];
         }
-        wave_lds_fence();
-
-        // S^T[key][query] for two 16-key blocks.
+        // S^T[key][query] for two 16-key blocks
         f32x4 sc[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             sc[mb] = f32x4{};
 #pragma unroll
-            for (int t = 0; t < C::KSTEPS; ++t) sc[mb] = mfma16(as_bf16x8(kcur[mb][t]), qf[t], sc[mb]);
+            for (int t = 0; t < C::KSTEPS; ++t) sc[mb] = mfma16(as_bf16x8(kr[mb * C::KSTEPS + t]), qf[t], sc[mb]);
         }
-        // Mask keys past the segment (only the last block can be short).
+        refill();  // this block's K registers are consumed; V is in LDS
+        wave_lds_fence();
+        // mask keys past the segment (only the last block can be short)
         const int key0 = k_beg + bi * KB;
         if (key0 + KB > k_end) {
 #pragma unroll
@@ -164,16 +164,21 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
                 for (int r = 0; r < 4; ++r)
                     if (key0 + 16 * mb + 4 * hq + r >= k_end) sc[mb][r] = -INFINITY;
         }
-
         float mx = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[mb][r]);
         mx = xor_max(xor_max(mx, 16), 32);
-        const float m_new = fmaxf(m2, mx * c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2_hw(m2 - m_use);
+        const float t_max = mx * c;
+        if (t_max > m2) {  // per lane: the decode state is tiny, rescale whenever the max grows
+            const float alpha = exp2_hw(m2 - t_max);  // 0 when m2 = -inf
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
+            m2 = t_max;
+        }
+        const float m_use = m2 == -INFINITY ? 0.f : m2;
         float ps = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -183,26 +188,32 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
                 sc[mb][r] = p;
                 ps += p;
             }
-        ps = xor_sum(xor_sum(ps, 16), 32);
-        lsum = fmaf(lsum, alpha, ps);
-        m2 = m_new;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
-
+        lsum += xor_sum(xor_sum(ps, 16), 32);
         // P^T as B operand: slot e <-> key 16*(e/4) + 4*hq + e%4.
         const bf16x8 pf = as_bf16x8(u32x4{pack_bf16x2(sc[0][0], sc[0][1]), pack_bf16x2(sc[0][2], sc[0][3]),
                                           pack_bf16x2(sc[1][0], sc[1][1]), pack_bf16x2(sc[1][2], sc[1][3])});
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) {
-            const uint16_t* vp = Vt + (16 * db + n16) * VS + 4 * hq;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
-            acc[db] = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf, acc[db]);
+            const i16x4 lo = lds_read_tr16(Vs + v_off[db]);
+            const i16x4 hi = lds_read_tr16(Vs + v_off[db] + 16 * D);
+            acc[db] = mfma16(__builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}),
+                             pf, acc[db]);
         }
-        wave_lds_fence();  // all lanes' reads of Vt done before the next block overwrites it
+        wave_lds_fence();  // every lane's reads of the V block are done before it is rewritten
+    };
+
+    // Two-slot register ring: while block i is computed, blocks i+NW and i+2*NW (this
+    // wave's next two) are in flight.
+    u32x4 k0[C::K_LOADS], v0[C::V_LOADS], k1[C::K_LOADS], v1[C::V_LOADS];
+    if (w < nblk) load_block(w, k0, v0);
+    if (w + NW < nblk) load_block(w + NW, k1, v1);
+    for (int bi = w; bi < nblk; bi += 2 * NW) {
+        compute(bi, k0, v0, [&] { if (bi + 2 * NW < nblk) load_block(bi + 2 * NW, k0, v0); });
+        if (bi + NW < nblk)
+            compute(bi + NW, k1, v1, [&] { if (bi + 3 * NW < nblk) load_block(bi + 3 * NW, k1, v1); });
     }
 
-    // Merge the 4 wave states through LDS (reusing the Vt space).
+    // Merge the 4 wave states through LDS (reusing the V blocks).
     __syncthreads();
     float* mm = reinterpret_cast<float*>(smem);  // [NW][NQ]
     float* ll = mm + NW * NQ;                    // [NW][NQ]
@@ -258,6 +269,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
 }
 
 // One wave per (b, h): lse = M + ln sum_s e^(lse_s - M); O = sum_s e^(lse_s - lse) o_s.
+// Lane t holds segment t's weight (t < 64 per pass); the o_s rows are then read with all
+// loads of a pass in flight and the weights broadcast from their lanes.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O_part,
                                                       const float* __restrict__ LSE_part,
@@ -282,10 +295,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         for (int k = 32; k >= 1; k >>= 1) sum = xor_sum(sum, k);
         lse = M + log2_hw(sum) * kLn2;
         const float* op = O_part + (int64_t)row * S * D + lane * DPL;
-        for (int t = 0; t < S; ++t) {
-            const float wgt = exp2_hw((lp[t] - lse) * kLog2e);  // 0 for an empty segment
+        for (int t0 = 0; t0 < S; t0 += 64) {
+            const int t = t0 + lane;
+            const float wl = t < S ? exp2_hw((lp[t] - lse) * kLog2e) : 0.f;  // 0 for empty segments
+            const int n = min(64, S - t0);
+            int u = 0;
+            for (; u + 8 <= n; u += 8) {
+                float x[8][DPL];
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) o[k] = fmaf(wgt, op[(int64_t)t * D + k], o[k]);
+                for (int a = 0; a < 8; ++a)
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k) x[a][k] = op[(int64_t)(t0 + u + a) * D + k];
+#pragma unroll
+                for (int a = 0; a < 8; ++a) {
+                    const float wgt = __shfl(wl, u + a, 64);
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k) o[k] = fmaf(wgt, x[a][k], o[k]);
+                }
+            }
+            for (; u < n; ++u) {
+                const float wgt = __shfl(wl, u, 64);
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) o[k] = fmaf(wgt, op[(int64_t)(t0 + u) * D + k], o[k]);
+            }
         }
     }
     uint16_t* dst = O + (int64_t)row * D + lane * DPL;
