@@ -230,7 +230,7 @@ def traffic_from_counters(dominant_kernel_substr):
     if c.get("kernel_source_hash") != kernel_source_hash():
         return None, "kernels changed since the counters were taken"
     for name, k in c.get("kernels", {}).items():
-        if name.startswith(dominant_kernel_substr):
+        if dominant_kernel_substr in name:
             return k.get("hbm_bytes_per_launch"), "profiles/hbm_counters.json (%s)" % name
     return None, "dominant kernel not in the counter summary"
 
@@ -239,11 +239,12 @@ def traffic_from_counters(dominant_kernel_substr):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--legs", default="fwd,decode,cpu", help="comma list of fwd, decode, cpu, copy")
     ap.add_argument("--all", action="store_true", help="also time the long-sequence and GQA forward workloads")
     ap.add_argument("--decode-reps", type=int, default=30)
+    ap.add_argument("--decode-nk", default="4096,65536", help="comma list of decode cache lengths")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
 
@@ -298,6 +299,8 @@ def main():
     if "decode" in legs:
         dec = {}
         for N_k, seed in ((4096, 5), (65536, 6)):
+            if str(N_k) not in args.decode_nk.split(","):
+                continue
             log("decode leg N_k=%d" % N_k)
             dec["N_k=%d" % N_k] = {k: (round(v, 2) if isinstance(v, float) else v)
                                    for k, v in leg_decode(fa, torch, args.decode_reps, N_k, seed).items()}

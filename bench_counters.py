@@ -7,6 +7,8 @@
     rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/write -o run -- \\
         python3 <repo>/bench.py --legs fwd,decode,copy --steps 3 --warmup 1 --decode-reps 3
     python3 <repo>/bench_counters.py OUT/fetch OUT/write
+    # or, with several runs (decode kernels of different cache lengths share one grid):
+    python3 <repo>/bench_counters.py N_k=4096=OUT/f4096,OUT/w4096 N_k=65536=OUT/f65536,OUT/w65536
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the L2 channels) are scaled by
 what the same counters read for the bench's plain 1 GiB device copy (`--legs copy`):
@@ -39,8 +41,9 @@ def kernel_key(name: str) -> str | None:
     return None
 
 
-def read_counter(run_dir: str, counter: str) -> dict:
-    per = defaultdict(lambda: defaultdict(float))
+def read_counter(run_dir: str, counter: str, label: str = "", per=None) -> dict:
+    """Average per dispatch of `counter`, keyed by kernel and grid (decode kernels also by label)."""
+    per = per if per is not None else defaultdict(lambda: defaultdict(float))
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit("no counter_collection.csv under %s" % run_dir)
@@ -52,17 +55,35 @@ def read_counter(run_dir: str, counter: str) -> dict:
             if key:
                 if key != "copy":
                     key += " grid=%s" % row["Grid_Size"]
-                per[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
+                    if label and not key.startswith("fwd_kernel"):
+                        key += " " + label
+                per[key][(f, row["Dispatch_Id"])] += float(row["Counter_Value"])
+    return per
+
+
+def averages(per) -> dict:
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
 def main():
-    if len(sys.argv) != 3:
+    args = sys.argv[1:]
+    if len(args) == 2 and "=" not in args[0]:
+        runs = [("", args[0], args[1])]
+    elif args and all("=" in a and "," in a for a in args):
+        runs = []
+        for a in args:
+            label, dirs = a.rsplit("=", 1)
+            f_dir, w_dir = dirs.split(",")
+            runs.append((label, f_dir, w_dir))
+    else:
         raise SystemExit(__doc__)
     import bench
 
-    fetch = read_counter(sys.argv[1], "FETCH_SIZE")
-    write = read_counter(sys.argv[2], "WRITE_SIZE")
+    fetch_per, write_per = None, None
+    for label, f_dir, w_dir in runs:
+        fetch_per = read_counter(f_dir, "FETCH_SIZE", label, fetch_per)
+        write_per = read_counter(w_dir, "WRITE_SIZE", label, write_per)
+    fetch, write = averages(fetch_per), averages(write_per)
     if "copy" not in fetch or "copy" not in write:
         raise SystemExit("the copy kernel is missing from the runs (use --legs ...,copy)")
     f_read = COPY_BYTES / (fetch["copy"] * 1024.0)
@@ -79,17 +100,20 @@ def main():
            "copy_fetch_kib": round(fetch["copy"], 1), "copy_write_kib": round(write["copy"], 1),
            "factor_read": round(f_read, 4), "factor_write": round(f_write, 4), "kernels": kernels,
            "command": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --kernel-trace --output-format csv -- "
-                      "python3 bench.py --legs fwd,decode,copy --steps 3 --warmup 1 --decode-reps 3"}
+                      "python3 bench.py --legs fwd,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3"}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "hbm_counters.json"), "w") as f:
         json.dump(out, f, indent=1)
     lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)", "",
-             "Commands (run from /tmp with TMPDIR=/tmp, one counter per run):", "",
-             "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/fetch -o run -- "
-             "python3 <repo>/bench.py --legs fwd,decode,copy --steps 3 --warmup 1 --decode-reps 3",
-             "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/write -o run -- "
-             "python3 <repo>/bench.py --legs fwd,decode,copy --steps 3 --warmup 1 --decode-reps 3",
-             "    python3 <repo>/bench_counters.py OUT/fetch OUT/write", "",
+             "Commands (run from /tmp with TMPDIR=/tmp, one counter per run, for each cache length NK "
+             "of the decode leg):", "",
+             "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/FETCH_SIZE_NK -o run -- "
+             "python3 <repo>/bench.py --legs fwd,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3",
+             "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/WRITE_SIZE_NK -o run -- "
+             "python3 <repo>/bench.py --legs fwd,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3",
+             "    python3 <repo>/bench_counters.py " + " ".join(
+                 "%s=OUT/FETCH_SIZE_%s,OUT/WRITE_SIZE_%s" % (lab, lab.split("=")[-1], lab.split("=")[-1])
+                 if lab else "OUT/fetch OUT/write" for lab, _, _ in runs), "",
              "Calibration: the bench's 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB, "
              "so counted reads are scaled by %.4f and writes by %.4f." % (fetch["copy"], write["copy"], f_read, f_write),
              "Kernel sources hash: `%s`." % out["kernel_source_hash"], "",
