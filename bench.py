@@ -129,8 +129,17 @@ def leg_forward_other(fa, torch, reps, name, seed, B, H, H_kv, N, d, causal):
     q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+    # Warm up for at least 30 ms of GPU time, so the clock has settled (it dips for about
+    # 10 ms after sustained load starts) before the timed launches.
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(torch.cuda.current_stream())
+    while True:
+        for _ in range(10):
+            fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        w1.record(torch.cuda.current_stream())
+        w1.synchronize()
+        if w0.elapsed_time(w1) >= 30.0:
+            break
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     stream = torch.cuda.current_stream()
     ev[0].record(stream)

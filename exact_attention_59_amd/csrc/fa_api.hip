@@ -68,7 +68,7 @@ FA_EXPORT const char* fa_strerror(int status) {
 FA_EXPORT int fa_fwd_tile_shape(int d, int* block_rows, int* block_cols) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (block_rows) *block_rows = fa::kFwdBlockRows;
-    if (block_cols) *block_cols = fa::kFwdBlockCols;
+    if (block_cols) *block_cols = fa::fwd_block_cols(d);
     return FA_OK;
 }
 
@@ -76,7 +76,7 @@ FA_EXPORT int fa_fwd_tile_shape(int d, int* block_rows, int* block_cols) {
 // n_i stops at the last key visible to the tile's last real row.
 FA_EXPORT long long fa_fwd_tile_count(int N_q, int N_k, int d, int causal) {
     if (N_q <= 0 || N_k <= 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1)) return -1;
-    const long long BR = fa::kFwdBlockRows, BC = fa::kFwdBlockCols;
+    const long long BR = fa::kFwdBlockRows, BC = fa::fwd_block_cols(d);
     const long long T_r = (N_q + BR - 1) / BR, T_c = (N_k + BC - 1) / BC;
     if (!causal) return T_r * T_c;
     long long total = 0;

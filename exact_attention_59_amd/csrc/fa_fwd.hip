@@ -46,7 +46,7 @@ namespace {
 template <int D>
 struct FwdCfg {
     static constexpr int BR = kFwdBlockRows;  // query rows per workgroup
-    static constexpr int BC = kFwdBlockCols;  // keys per tile
+    static constexpr int BC = fwd_block_cols(D);  // keys per tile
     static constexpr int THREADS = 256;
     static constexpr int TILE = BC * D;       // elements of one K or V tile buffer (rows unpadded)
     // A 64-lane global->LDS copy moves 1 KB; the 4 waves split a tile's copies evenly.
@@ -64,9 +64,23 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained): this wave's global->LDS
-// copies have landed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Copy 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at LDS byte address lds_base + 16 * l.  Issued as inline assembly so
+// that the compiler's wait-count bookkeeping does not see it: the compiler counts such a
+// copy as both a vector-memory and an LDS access, which would turn every LDS-read wait in
+// the loop into a full wait.  Completion is awaited explicitly with wait_vmem(), and the
+// workgroup barrier after that orders it before any read of the buffer.
+__device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+
+// s_waitcnt vmcnt(0): this wave's global->LDS copies have landed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
 
 // Lazy rescale threshold (log2 units).  The running max m is only moved when a tile's
 // max exceeds it by more than this; until then p = 2^(t - m) <= 2^kRescaleSlack, which
@@ -111,6 +125,11 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[C::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[C::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[C::TILE];
+
+    // The output pointers are first needed after the loop; consume their scalar loads
+    // here.  A scalar load still in flight would make every LDS wait in the loop a full
+    // wait (scalar and LDS loads share one counter, and scalar ones complete out of order).
+    asm volatile("" ::"s"(O), "s"(LSE));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -163,6 +182,7 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     constexpr int ROWS_PER_COPY = 512 / D;
     const int dma_r0 = w * C::DMA_PER_WAVE * ROWS_PER_COPY + lane / (D / 8);
     const int dma_sc = lane % (D / 8);
+    const uint32_t dma_lds_off = __builtin_amdgcn_readfirstlane(w * C::DMA_PER_WAVE * 1024);  // bytes
     auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* dst, bool is_v) {
         const int key0 = j * BC;
         const uint16_t* head = src + kv_base;
@@ -171,9 +191,7 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
             const int r = dma_r0 + t * ROWS_PER_COPY;
             const int c = dma_sc ^ (is_v ? swz_v<D>(r) : swz_k<D>(r));
             const uint16_t* g = head + (int64_t)min(key0 + r, N_k - 1) * D + 8 * c;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(g),
-                (__attribute__((address_space(3))) void*)(dst + (w * C::DMA_PER_WAVE + t) * 512), 16, 0, 0);
+            copy_to_lds16(g, lds_addr(dst) + dma_lds_off + t * 1024);
         }
     };
 
@@ -187,14 +205,23 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = l32 * D + 8 * ((2 * ks + hh) ^ sk);
     }
-    auto qk = [&](const uint16_t* Ks, f32x16 (&s)[BC / 32]) {
+    // Fragments are read from LDS into registers at the top of a step, all at once, so
+    // their latency overlaps the softmax instead of stalling each MFMA.
+    using KFrag = bf16x8[D / 16][BC / 32];
+    auto load_k = [&](const uint16_t* Ks, KFrag& kf) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < BC / 32; ++mb)
+                kf[ks][mb] = *reinterpret_cast<const bf16x8*>(Ks + k_off[ks] + 32 * mb * D);
+    };
+    auto qk = [&](const KFrag& kf, f32x16 (&s)[BC / 32]) {
 #pragma unroll
         for (int mb = 0; mb < BC / 32; ++mb) s[mb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-            for (int mb = 0; mb < BC / 32; ++mb)
-                s[mb] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + k_off[ks] + 32 * mb * D), qf[ks], s[mb]);
+            for (int mb = 0; mb < BC / 32; ++mb) s[mb] = mfma32(kf[ks][mb], qf[ks], s[mb]);
     };
     // O^T[d][query] += V_j^T P^T.  P^T is the B operand: for 16-key step k2, half hh of
     // the wave holds keys 16*k2 + 4*hh + (0..3) and 16*k2 + 8 + 4*hh + (0..3).  The A
@@ -217,17 +244,25 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
         for (int db = 0; db < D / 32; ++db)
             v_off[db] = (4 * hh + (i >> 2)) * D + 32 * (db ^ sv) + 8 * cg + 4 * (i & 1);
     }
-    auto pv = [&](const uint16_t* Vs, const bf16x8 (&pf)[BC / 16]) {
+    // V^T fragments of 16-key steps k2 in [K2_0, K2_1).
+    using VFrag = i16x8[BC / 16][D / 32];
+    auto load_v = [&](const uint16_t* Vs, VFrag& vf, auto k2_0, auto k2_1) {
 #pragma unroll
-        for (int k2 = 0; k2 < BC / 16; ++k2)
+        for (int k2 = decltype(k2_0)::value; k2 < decltype(k2_1)::value; ++k2)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 const uint16_t* p = Vs + v_off[db] + 16 * k2 * D;
                 const i16x4 lo = lds_read_tr16(p);
                 const i16x4 hi = lds_read_tr16(p + 8 * D);
-                acc[db] = mfma32(__builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}),
-                                 pf[k2], acc[db]);
+                vf[k2][db] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
+    };
+    auto pv = [&](const VFrag& vf, const bf16x8 (&pf)[BC / 16]) {
+#pragma unroll
+        for (int k2 = 0; k2 < BC / 16; ++k2)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                acc[db] = mfma32(__builtin_bit_cast(bf16x8, vf[k2][db]), pf[k2], acc[db]);
     };
 
     // ---- online softmax state of this lane's query row (both 32-lane halves hold it)
@@ -303,7 +338,9 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
         wait_vmem();
         __syncthreads();
         // Unconditional (a wave with no rows to compute ignores the result).
-        qk(k_lds0, sA);
+        KFrag kf;
+        load_k(k_lds0, kf);
+        qk(kf, sA);
         __syncthreads();
     }
 
@@ -316,14 +353,30 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
         if (j + 2 < n_tiles) dma_tile(K, j + 2, k_fill, false);
         if (j + 1 < n_tiles) dma_tile(V, j + 1, v_fill, true);
         if (j < n_w) {
-            const float m_use = softmax_prepare(s_cur, j);
             bf16x8 pf[BC / 16];
-            // Tile j+1's scores, issued unconditionally so that the MFMAs share a basic
-            // block with the exps below and overlap them.  Past this wave's last tile the
-            // buffer holds other finite data and the result is never used.
-            qk(k_read, s_next);
-            softmax_finish(s_cur, m_use, pf);
-            pv(v_read, pf);
+            KFrag kf;
+            VFrag vf;
+            if constexpr (D == 64) {
+                // All fragments of K_{j+1} and V_j^T are requested before any arithmetic,
+                // so their latency overlaps the softmax instead of stalling each MFMA.
+                load_k(k_read, kf);
+                load_v(v_read, vf, std::integral_constant<int, 0>{}, std::integral_constant<int, BC / 16>{});
+                __builtin_amdgcn_sched_barrier(0);
+                const float m_use = softmax_prepare(s_cur, j);
+                // Tile j+1's scores, issued unconditionally so that the MFMAs share a basic
+                // block with the exps below and overlap them.  Past this wave's last tile the
+                // buffer holds other finite data and the result is never used.
+                qk(kf, s_next);
+                softmax_finish(s_cur, m_use, pf);
+                pv(vf, pf);
+            } else {
+                const float m_use = softmax_prepare(s_cur, j);
+                load_k(k_read, kf);
+                qk(kf, s_next);
+                softmax_finish(s_cur, m_use, pf);
+                load_v(v_read, vf, std::integral_constant<int, 0>{}, std::integral_constant<int, BC / 16>{});
+                pv(vf, pf);
+            }
         }
         wait_vmem();
         __syncthreads();

@@ -7,10 +7,10 @@
 
 namespace fa {
 
-// Forward tile shape (query rows per workgroup, keys per tile); both head dimensions
-// use the same shape.
+// Forward tile shape: query rows per workgroup, and keys per tile for head dimension d
+// (the same for both head dimensions).
 constexpr int kFwdBlockRows = 128;
-constexpr int kFwdBlockCols = 64;
+constexpr int fwd_block_cols(int /*d*/) { return 64; }
 
 // Decode: keys per wave iteration and query heads per workgroup.
 constexpr int kDecKeysPerWave = 32;

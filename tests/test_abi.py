@@ -128,8 +128,9 @@ def test_num_splits_range(lib):
 
 
 def test_tile_shape(lib):
-    assert fa.fwd_tile_shape(64) == fa.fwd_tile_shape(128)
-    br, bc = fa.fwd_tile_shape(128)
-    assert br % 32 == 0 and bc % 32 == 0
+    # whole 32-row blocks per wave and whole 32-key MFMA blocks per tile
+    for d in (64, 128):
+        br, bc = fa.fwd_tile_shape(d)
+        assert br % 32 == 0 and bc % 32 == 0
     with pytest.raises(fa.FAError):
         fa.fwd_tile_shape(96)
