@@ -188,9 +188,48 @@ def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=
     split = sorted(e[0].elapsed_time(e[1]) for e in evs)
     comb = sorted(e[1].elapsed_time(e[2]) for e in evs)
     both = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    # For comparison (information only): the unsplit forward with N_q = 1 on the same shapes,
+    # one workgroup per (b, h), reading each K/V head once per query head of its group.
+    q4 = q.view(B, H, 1, d)
+    o4 = torch.empty_like(q4)
+    lse4 = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
+    fa.fwd(q4, k, v, causal=False, out=o4, lse=lse4)
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        torch.amax(flush)
+        evf[i][0].record(stream)
+        fa.fwd(q4, k, v, causal=False, out=o4, lse=lse4)
+        evf[i][1].record(stream)
+    torch.cuda.synchronize()
+    unsplit_ms = sum(e[0].elapsed_time(e[1]) for e in evf) / reps
+    # Paged cache (16-token pages, shuffled over the pool, every sequence full length): the
+    # same split through a block table.
+    P = 16
+    npp = N_k // P
+    perm = torch.randperm(B * npp, generator=torch.Generator().manual_seed(seed)).cuda()
+    def to_pages(x):  # [B,H_kv,N_k,d] -> pool [B*npp, H_kv, P, d], logical page i of b at perm[b*npp+i]
+        logical = x.view(B, H_kv, npp, P, d).permute(0, 2, 1, 3, 4).reshape(B * npp, H_kv, P, d)
+        pool = torch.empty_like(logical)
+        pool[perm] = logical
+        return pool
+    kp, vp = to_pages(k), to_pages(v)
+    table = perm.view(B, npp).to(torch.int32).contiguous()
+    lens = torch.full((B,), N_k, dtype=torch.int32, device="cuda")
+    fa.decode_split_paged(q, kp, vp, table, lens, S, o_part=o_part, lse_part=l_part)
+    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        torch.amax(flush)
+        evp[i][0].record(stream)
+        fa.decode_split_paged(q, kp, vp, table, lens, S, o_part=o_part, lse_part=l_part)
+        evp[i][1].record(stream)
+    torch.cuda.synchronize()
+    paged_ms = sum(e[0].elapsed_time(e[1]) for e in evp) / reps
+    del kp, vp
     ms = sum(split) / reps
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     return {"N_k": N_k, "num_splits": S, "split_us": ms * 1e3, "split_us_median": split[reps // 2] * 1e3,
+            "paged16_split_us": paged_ms * 1e3, "paged16_split_GBs": kv_bytes / (paged_ms * 1e-3) / 1e9,
+            "unsplit_fwd_us": unsplit_ms * 1e3, "unsplit_fwd_GBs": kv_bytes / (unsplit_ms * 1e-3) / 1e9,
             "combine_us": sum(comb) / reps * 1e3, "end_to_end_us": sum(both) / reps * 1e3,
             "split_GBs": gbs, "split_pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS,
             "end_to_end_GBs": kv_bytes / (sum(both) / reps * 1e-3) / 1e9, "kv_bytes": kv_bytes}

@@ -17,7 +17,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "decode_split", "combine", "decode", "decode_num_splits", "decode_workspace_bytes",
+__all__ = ["fwd", "decode_split", "decode_split_paged", "combine", "decode", "decode_num_splits",
+           "decode_workspace_bytes",
            "fwd_tile_shape", "fwd_tile_count", "strerror", "library", "library_path", "FAError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,8 @@ def library():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
         lib.fa_decode_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                              f32, vp]
         lib.fa_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
         lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
         lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -57,7 +60,7 @@ def library():
         lib.fa_fwd_tile_count.restype = ctypes.c_longlong
         lib.fa_strerror.argtypes = [i32]
         lib.fa_strerror.restype = ctypes.c_char_p
-        for fn in (lib.fa_fwd, lib.fa_decode_split, lib.fa_combine, lib.fa_decode_num_splits,
+        for fn in (lib.fa_fwd, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits,
                    lib.fa_fwd_tile_shape):
             fn.restype = i32
         _lib = lib
@@ -154,6 +157,43 @@ def decode_split(q, k, v, num_splits: int, scale: float | None = None, o_part=No
     _check("fa_decode_split",
            library().fa_decode_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
                                      lse_part.data_ptr(), B, H, H_kv, N_k, d, S, float(scale), _stream_ptr(q)))
+    return o_part, lse_part
+
+
+def decode_split_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits: int, scale: float | None = None,
+                       o_part=None, lse_part=None):
+    """fa_decode_split_paged.  q [B,H,d] bf16; k/v pages [num_pages,H_kv,P,d] bf16; block_table
+    [B,max_pages] int32; seq_lens [B] int32 -> o_part [B,H,S,d], lse_part [B,H,S] fp32."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, H, d = q.shape
+    num_pages, H_kv, P, dk = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or dk != d:
+        raise ValueError("shape mismatch: q %s k_pages %s v_pages %s" % (tuple(q.shape), tuple(k_pages.shape),
+                                                                      tuple(v_pages.shape)))
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    max_pages = block_table.shape[1]
+    S = int(num_splits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o_part is None:
+        o_part = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32, 4)
+    _need(lse_part, "lse_part", torch.float32, 3)
+    if tuple(o_part.shape) != (B, H, S, d) or tuple(lse_part.shape) != (B, H, S):
+        raise ValueError("partial output shapes do not match")
+    _check("fa_decode_split_paged",
+           library().fa_decode_split_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                           block_table.data_ptr(), seq_lens.data_ptr(), o_part.data_ptr(),
+                                           lse_part.data_ptr(), B, H, H_kv, P, max_pages, num_pages, d, S,
+                                           float(scale), _stream_ptr(q)))
     return o_part, lse_part
 
 

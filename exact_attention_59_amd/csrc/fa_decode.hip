@@ -48,14 +48,26 @@ struct DecCfg {
 template <int D>
 __device__ __forceinline__ int dec_swz(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
-template <int D>
+// Paged key/value cache (PAGED = true): K and V are pools of pages [num_pages][H_kv][P][D]
+// (P = 2^page_log2 >= 16 tokens of one head contiguous in a page); token t of sequence b
+// lives in page block_table[b][t / P] at row t % P; seq_lens[b] tokens are valid.  A
+// 32-key block starts at a multiple of 16 tokens, so each of its two 16-key halves lies in
+// one page.  Lengths and table entries are clamped to the pool, so a bad table cannot
+// address memory outside it.
+struct PagedKV {
+    const int* block_table;  // [B][max_pages]
+    const int* seq_lens;     // [B]
+    int page_log2, max_pages, num_pages;
+};
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __restrict__ Q,
                                                               const uint16_t* __restrict__ K,
                                                               const uint16_t* __restrict__ V,
                                                               float* __restrict__ O_part,
                                                               float* __restrict__ LSE_part, int H,
                                                               int H_kv, int N_k, int S, int L, int n_qc,
-                                                              float c) {
+                                                              float c, PagedKV pg) {
     using C = DecCfg<D>;
     constexpr int KB = C::KB, NQ = C::NQ, NW = C::NW, CPR = C::CPR;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM_BYTES];
@@ -71,9 +83,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
     const int group = H / H_kv;
     const int b = bg / H_kv, g = bg - b * H_kv;
 
-    const int k_beg = min(s * L, N_k), k_end = min(k_beg + L, N_k);
+    // Keys [k_beg, k_end) of this sequence form segment s.  Paged: per-sequence length, and
+    // segment lengths rounded up to whole 32-key blocks (so blocks start on 16-token rows).
+    int len = N_k, seg = L;
+    if constexpr (PAGED) {
+        len = min(max(pg.seq_lens[b], 0), pg.max_pages << pg.page_log2);
+        seg = ((len + S - 1) / S + KB - 1) / KB * KB;
+    }
+    const int k_beg = min(s * seg, len), k_end = min(k_beg + seg, len);
     const int nblk = (k_end - k_beg + KB - 1) / KB;
-    const uint16_t* Kh = K + (int64_t)bg * N_k * D;
+    const uint16_t* Kh = K + (int64_t)bg * N_k * D;  // contiguous layout
     const uint16_t* Vh = V + (int64_t)bg * N_k * D;
 
     // Query head of this lane's MFMA column.
@@ -96,16 +115,37 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
 
     // ---- block loads.  K: lane (n16, hq) holds row 16*mb + n16, d = 32*t + 8*hq + 0..7
     // (the 4 lanes of a row cover one 64-byte line per instruction).  V: lane holds row
-    // v_kg*V_LOADS + r, chunk v_dc.  Rows past the segment read as zero.
+    // v_kg*V_LOADS + r, chunk v_dc (V_LOADS divides 16: a lane's rows share a 16-key half).
+    // Rows past the segment read as zero, from a clamped in-bounds address.
     const int v_dc = lane % CPR, v_kg = lane / CPR;
+    static_assert(16 % C::V_LOADS == 0, "a lane's V rows stay in one 16-key half");
     auto load_block = [&](int bi, u32x4 (&kr)[C::K_LOADS], u32x4 (&vr)[C::V_LOADS]) {
         const int key0 = k_beg + bi * KB;
         const bool full = key0 + KB <= k_end;
+        // Row key0 + 16*half of K and V (half = 0, 1).
+        const uint16_t *kh0, *kh1, *vh0, *vh1;
+        if constexpr (PAGED) {
+            const int P = 1 << pg.page_log2;
+            const int* bt = pg.block_table + (int64_t)b * pg.max_pages;
+            const int p0 = min(max(bt[key0 >> pg.page_log2], 0), pg.num_pages - 1);
+            const int p1 = min(max(bt[min((key0 + 16) >> pg.page_log2, pg.max_pages - 1)], 0), pg.num_pages - 1);
+            const int64_t o0 = (((int64_t)p0 * H_kv + g) * P + (key0 & (P - 1))) * D;
+            const int64_t o1 = (((int64_t)p1 * H_kv + g) * P + ((key0 + 16) & (P - 1))) * D;
+            kh0 = K + o0;
+            kh1 = K + o1;
+            vh0 = V + o0;
+            vh1 = V + o1;
+        } else {
+            kh0 = Kh + (int64_t)key0 * D;
+            kh1 = kh0 + 16 * D;
+            vh0 = Vh + (int64_t)key0 * D;
+            vh1 = vh0 + 16 * D;
+        }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const int key = key0 + 16 * mb + n16;
-            const int key_c = full ? key : min(key, N_k - 1);  // in-bounds address
-            const u32x4* kp = reinterpret_cast<const u32x4*>(Kh + (int64_t)key_c * D + 8 * hq);
+            const int rel = (full ? key : min(key, k_end - 1)) - key0;  // in-bounds row
+            const u32x4* kp = reinterpret_cast<const u32x4*>((rel >= 16 ? kh1 : kh0) + (rel & 15) * D + 8 * hq);
 #pragma unroll
             for (int t = 0; t < C::KSTEPS; ++t)
                 kr[mb * C::KSTEPS + t] = (full || key < k_end) ? kp[4 * t] : u32x4{0, 0, 0, 0};
@@ -113,9 +153,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
 #pragma unroll
         for (int r = 0; r < C::V_LOADS; ++r) {
             const int key = key0 + v_kg * C::V_LOADS + r;
-            const int key_c = full ? key : min(key, N_k - 1);
-            vr[r] = (full || key < k_end) ? *reinterpret_cast<const u32x4*>(Vh + (int64_t)key_c * D + v_dc * 8)
-                                          : u32x4{0, 0, 0, 0};
+            const int rel = (full ? key : min(key, k_end - 1)) - key0;
+            vr[r] = (full || key < k_end)
+                        ? *reinterpret_cast<const u32x4*>((rel >= 16 ? vh1 : vh0) + (rel & 15) * D + v_dc * 8)
+                        : u32x4{0, 0, 0, 0};
         }
     };
 
@@ -330,17 +371,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (LSE && lane == 0) LSE[row] = lse;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_decode_t(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
-                           int B, int H, int H_kv, int N_k, int S, float scale, hipStream_t stream) {
+                           int B, int H, int H_kv, int N_k, int S, float scale, const PagedKV& pg,
+                           hipStream_t stream) {
     const int group = H / H_kv;
     const int n_qc = (group + kDecHeadsPerBlock - 1) / kDecHeadsPerBlock;
     const int L = (N_k + S - 1) / S;
     const float c = (float)((double)scale * 1.4426950408889634073599);
     const long long blocks = (long long)S * n_qc * B * H_kv;
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-                       static_cast<const uint16_t*>(V), O_part, LSE_part, H, H_kv, N_k, S, L, n_qc, c);
+                       static_cast<const uint16_t*>(V), O_part, LSE_part, H, H_kv, N_k, S, L, n_qc, c, pg);
     return hipGetLastError();
 }
 
@@ -358,9 +400,25 @@ hipError_t launch_combine_t(const float* O_part, const float* LSE_part, void* O,
 hipError_t launch_decode_split(const void* Q, const void* K, const void* V, float* O_part,
                                float* LSE_part, int B, int H, int H_kv, int N_k, int d, int num_splits,
                                float scale, hipStream_t stream) {
+    const PagedKV none{nullptr, nullptr, 0, 0, 0};
     if (d == 64)
-        return launch_decode_t<64>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale, stream);
-    return launch_decode_t<128>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale, stream);
+        return launch_decode_t<64, false>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale, none,
+                                          stream);
+    return launch_decode_t<128, false>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale, none,
+                                       stream);
+}
+
+hipError_t launch_decode_split_paged(const void* Q, const void* K_pages, const void* V_pages,
+                                     const int* block_table, const int* seq_lens, float* O_part,
+                                     float* LSE_part, int B, int H, int H_kv, int page_log2, int max_pages,
+                                     int num_pages, int d, int num_splits, float scale, hipStream_t stream) {
+    const PagedKV pg{block_table, seq_lens, page_log2, max_pages, num_pages};
+    // N_k = 0: the contiguous layout is not used
+    if (d == 64)
+        return launch_decode_t<64, true>(Q, K_pages, V_pages, O_part, LSE_part, B, H, H_kv, 0, num_splits, scale,
+                                         pg, stream);
+    return launch_decode_t<128, true>(Q, K_pages, V_pages, O_part, LSE_part, B, H, H_kv, 0, num_splits, scale,
+                                      pg, stream);
 }
 
 hipError_t launch_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,

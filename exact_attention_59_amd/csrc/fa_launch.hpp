@@ -23,6 +23,11 @@ hipError_t launch_decode_split(const void* Q, const void* K, const void* V, floa
                                float* LSE_part, int B, int H, int H_kv, int N_k, int d, int num_splits,
                                float scale, hipStream_t stream);
 
+hipError_t launch_decode_split_paged(const void* Q, const void* K_pages, const void* V_pages,
+                                     const int* block_table, const int* seq_lens, float* O_part,
+                                     float* LSE_part, int B, int H, int H_kv, int page_log2, int max_pages,
+                                     int num_pages, int d, int num_splits, float scale, hipStream_t stream);
+
 hipError_t launch_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,
                           int d, int num_splits, hipStream_t stream);
 

@@ -8,6 +8,8 @@
  *   fa_decode_split  flash-decoding, step 2: one query token per sequence, keys cut
  *                    into num_splits contiguous segments, per-segment normalised
  *                    output o_s and lse_s.
+ *   fa_decode_split_paged  the split step over a paged key/value cache
+ *                    (block table, per-sequence lengths).
  *   fa_combine       flash-decoding, step 3: exact merge of the segments by
  *                    log-sum-exp.
  * Sources: Lecture 11, "Kernel Optimization Techniques: FlashAttention,
@@ -88,6 +90,35 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
  */
 int fa_decode_split(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
                     int B, int H, int H_kv, int N_k, int d, int num_splits, float scale, void* stream);
+
+/*
+ * Flash-decoding split step over a paged key/value cache (Lecture 11, the
+ * flash-decoding section and "State of the field": paged KV needs the attention
+ * kernel to address keys indirectly through a block table).  Same computation as
+ * fa_decode_split for sequence b over its first seq_lens[b] cached tokens, which
+ * are scattered over fixed-size pages:
+ *   Q           [B][H][d]                          bf16, read
+ *   K_pages,
+ *   V_pages     [num_pages][H_kv][page_size][d]    bf16, read: page p holds
+ *               page_size consecutive tokens of every key/value head
+ *   block_table [B][max_pages]                     int32, read: token t of sequence b
+ *               is row t % page_size of page block_table[b][t / page_size]
+ *   seq_lens    [B]                                int32, read: valid tokens per sequence
+ *   O_part, LSE_part as for fa_decode_split.
+ * Segment s of sequence b covers tokens [s*L_b, min((s+1)*L_b, seq_lens[b])), with
+ * L_b = ceil(seq_lens[b] / num_splits) rounded up to a multiple of 32; later
+ * segments may be empty (o_s = 0, lse_s = -inf), and a sequence of length 0 gives
+ * O = 0, LSE = -inf after fa_combine.  Device-side values are not validated:
+ * seq_lens[b] is clamped to [0, max_pages * page_size] and table entries to
+ * [0, num_pages - 1], so a bad table cannot make the kernel read outside the pools.
+ * block_table and seq_lens must be 4-byte aligned; the other pointers 16-byte.
+ * Limits: d in {64, 128}; H / H_kv <= 64; page_size a power of two in
+ * [16, 4096]; num_splits in [1, max_pages * page_size].
+ */
+int fa_decode_split_paged(const void* Q, const void* K_pages, const void* V_pages,
+                          const int* block_table, const int* seq_lens, float* O_part,
+                          float* LSE_part, int B, int H, int H_kv, int page_size, int max_pages,
+                          int num_pages, int d, int num_splits, float scale, void* stream);
 
 /*
  * Flash-decoding combine (Lecture 11 section 6.2, step 3): per (b, h),

@@ -37,7 +37,7 @@ def exported_symbols(path):
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_decode_split", "fa_combine", "fa_decode_num_splits",
+    for want in ("fa_fwd", "fa_decode_split", "fa_decode_split_paged", "fa_combine", "fa_decode_num_splits",
                  "fa_decode_workspace_bytes", "fa_strerror", "fa_fwd_tile_shape", "fa_fwd_tile_count"):
         assert want in names
 
@@ -94,6 +94,37 @@ def test_fwd_validation(lib, kw, status):
 ])
 def test_decode_validation(lib, kw, status):
     assert dec(lib, **kw) == status
+
+
+def paged(lib, Q=P, K=P, V=P, T=P, Ls=P, Op=P, Lp=P, B=2, H=4, H_kv=1, page=16, max_pages=8, num_pages=16,
+          d=128, S=4, scale=0.1):
+    return lib.fa_decode_split_paged(Q, K, V, T, Ls, Op, Lp, B, H, H_kv, page, max_pages, num_pages, d, S, scale,
+                                     None)
+
+
+P_INT = ctypes.c_void_p(0x100004)   # 4-byte aligned: fine for the int32 arrays
+P_ODD = ctypes.c_void_p(0x100002)   # 2-byte aligned
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(T=None), fa.FA_ERR_NULL), (dict(Ls=None), fa.FA_ERR_NULL),
+    (dict(K=None), fa.FA_ERR_NULL), (dict(Lp=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(page=0), fa.FA_ERR_SHAPE), (dict(max_pages=0), fa.FA_ERR_SHAPE),
+    (dict(num_pages=-1), fa.FA_ERR_SHAPE), (dict(H=5, H_kv=2), fa.FA_ERR_SHAPE),
+    (dict(S=0), fa.FA_ERR_SHAPE), (dict(S=16 * 8 + 1), fa.FA_ERR_SHAPE),
+    (dict(page=24), fa.FA_ERR_UNSUPPORTED), (dict(page=8), fa.FA_ERR_UNSUPPORTED),
+    (dict(page=8192), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=65, H_kv=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(K=P_MIS), fa.FA_ERR_ALIGN), (dict(T=P_ODD), fa.FA_ERR_ALIGN), (dict(Ls=P_ODD), fa.FA_ERR_ALIGN),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG),
+])
+def test_decode_paged_validation(lib, kw, status):
+    assert paged(lib, **kw) == status
+
+
+def test_decode_paged_int_pointers_need_only_4_bytes(lib):
+    # 4-byte aligned table and lengths pass the alignment check (a later check fails instead)
+    assert paged(lib, T=P_INT, Ls=P_INT, S=0) == fa.FA_ERR_SHAPE
 
 
 @pytest.mark.parametrize("kw,status", [
