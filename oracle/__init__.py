@@ -13,6 +13,8 @@ Techniques: FlashAttention, flash-decoding and megakernel"):
   online_row    one-pass online softmax times V (section 3.1).
   merge         merge of partial states (m, l, o) (section 3.2).
   lse_combine   flash-decoding combine in LSE form (section 6.2).
+  attention_bwd gradients of sum(dO * O) w.r.t. Q, K, V from the full P
+                (section 5.1, the standard backward).
 
 Parity pins: every function above is pinned by tests against facts the pages
 or the mathematics fix (worked Exercise 1, closed forms, brute force in
@@ -74,6 +76,9 @@ class Oracle:
         lib.oracle_merge.restype = None
         lib.oracle_lse_combine.argtypes = [vp, vp, i64, i64, vp, vp]
         lib.oracle_lse_combine.restype = None
+        lib.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, i32, d64,
+                                             vp, vp, vp, vp, i32]
+        lib.oracle_attention_bwd.restype = i32
         self.lib = lib
 
     # ------------------------------------------------------------------ Algorithm 0
@@ -159,6 +164,34 @@ class Oracle:
         return lse.value, out[:d]
 
 
+    # ------------------------------------------------------------------ backward
+    def attention_bwd(self, Q, K, V, dO, causal=False, scale=None, nthreads=None):
+        """Gradients of sum(dO * O).  Q, dO [B,H,N_q,d], K/V [B,H_kv,N_k,d] (one shared dtype).
+
+        Returns (dQ [B,H,N_q,d], dK [B,H_kv,N_k,d], dV [B,H_kv,N_k,d], D [B,H,N_q]) in fp64.
+        """
+        Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
+        if not (Q.dtype == K.dtype == V.dtype == dO.dtype) or Q.dtype not in _DTYPES:
+            raise TypeError("Q, K, V, dO must share one of uint16 (bf16), float32, float64")
+        B, H, N_q, d = Q.shape
+        Bk, H_kv, N_k, dk = K.shape
+        if V.shape != K.shape or Bk != B or dk != d or dO.shape != Q.shape:
+            raise ValueError("shape mismatch")
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        dQ = np.empty((B, H, N_q, d))
+        dK = np.empty((B, H_kv, N_k, d))
+        dV = np.empty((B, H_kv, N_k, d))
+        D = np.empty((B, H, N_q))
+        rc = self.lib.oracle_attention_bwd(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dO.ctypes.data,
+                                           _DTYPES[Q.dtype], B, H, H_kv, N_q, N_k, d, int(bool(causal)),
+                                           float(scale), dQ.ctypes.data, dK.ctypes.data, dV.ctypes.data,
+                                           D.ctypes.data, host_threads() if nthreads is None else int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_attention_bwd failed with code %d" % rc)
+        return dQ, dK, dV, D
+
+
 _default = None
 
 
@@ -183,3 +216,7 @@ def merge(*args, **kwargs):
 
 def lse_combine(*args, **kwargs):
     return default().lse_combine(*args, **kwargs)
+
+
+def attention_bwd(*args, **kwargs):
+    return default().attention_bwd(*args, **kwargs)

@@ -25,6 +25,10 @@
  *   oracle_merge       merge of two partial states (m, l, o) (section 3.2).
  *   oracle_lse_combine flash-decoding's combine in log-sum-exp form
  *                      (section 6.2, step 3).
+ *   oracle_attention_bwd the backward pass (section 5.1): gradients of
+ *                      sum(dO * O) with respect to Q, K, V from the full
+ *                      probability matrix P (the "standard" backward that the
+ *                      section compares FlashAttention's against).
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - layout: Q [B][H][N_q][d], K and V [B][H_kv][N_k][d], row-major;
@@ -282,4 +286,125 @@ void oracle_lse_combine(const double* lse_s, const double* o_s, int64_t S, int64
         for (int64_t k = 0; k < d; ++k) o_out[k] += w * o_s[t * d + k];
     }
     *lse_out = lse;
+}
+
+/*
+ * Backward pass of exact attention (Lecture 11 section 5.1), the standard form that
+ * works from the full rows of P.  With S = scale * Q K^T, P = softmax(S) over the
+ * visible keys and O = P V, the gradients of the scalar sum(dO * O) are
+ *   dV = P^T dO,   dP = dO V^T,   D_i = sum_j dP_ij P_ij,   dS = P * (dP - D),
+ *   dQ = scale * dS K,   dK = scale * dS^T Q
+ * (the softmax Jacobian applied to dP gives dS; the section's D_i).  Gradients of a
+ * key/value head collect every query head of its group.  Same layouts, masking and
+ * element types as oracle_attention; outputs are fp64: dQ [B][H][N_q][d],
+ * dK and dV [B][H_kv][N_k][d], and D [B][H][N_q] if D is not NULL.
+ * Returns 0, or -1 on a bad argument, -2 if memory ran out.
+ */
+typedef struct {
+    const void *Q, *K, *V, *dO;
+    int dtype;
+    int64_t B, H, H_kv, N_q, N_k, d;
+    int causal;
+    double scale;
+    double *dQ, *dK, *dV, *D;
+    int64_t next; /* shared counter over (b, key/value head) jobs */
+} bwd_job;
+
+static void bwd_group(const bwd_job* a, int64_t bg, double* p, double* dp) {
+    const int64_t d = a->d, N_q = a->N_q, N_k = a->N_k;
+    const int64_t b = bg / a->H_kv, g = bg % a->H_kv;
+    const int64_t group = a->H / a->H_kv;
+    const int64_t kv_head = bg * N_k;
+    double* dK = a->dK + kv_head * d;
+    double* dV = a->dV + kv_head * d;
+    for (int64_t t = 0; t < N_k * d; ++t) dK[t] = dV[t] = 0.0;
+    for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+        for (int64_t i = 0; i < N_q; ++i) {
+            const int64_t r = (b * a->H + h) * N_q + i;
+            const int64_t q_off = r * d;
+            double* dq = a->dQ + q_off;
+            for (int64_t k = 0; k < d; ++k) dq[k] = 0.0;
+            int64_t j_end = N_k;
+            if (a->causal) {
+                int64_t last = i + N_k - N_q;
+                if (last + 1 < j_end) j_end = last + 1;
+            }
+            if (j_end <= 0) {
+                if (a->D) a->D[r] = 0.0;
+                continue;
+            }
+            /* P row: scores, safe softmax */
+            for (int64_t j = 0; j < j_end; ++j) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < d; ++k)
+                    acc += widen(a->Q, a->dtype, q_off + k) * widen(a->K, a->dtype, (kv_head + j) * d + k);
+                p[j] = a->scale * acc;
+            }
+            double m = p[0];
+            for (int64_t j = 1; j < j_end; ++j)
+                if (p[j] > m) m = p[j];
+            double l = 0.0;
+            for (int64_t j = 0; j < j_end; ++j) {
+                p[j] = exp(p[j] - m);
+                l += p[j];
+            }
+            for (int64_t j = 0; j < j_end; ++j) p[j] /= l;
+            /* dP row = dO_i V^T, and D_i = sum_j dP_ij P_ij */
+            double Di = 0.0;
+            for (int64_t j = 0; j < j_end; ++j) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < d; ++k)
+                    acc += widen(a->dO, a->dtype, q_off + k) * widen(a->V, a->dtype, (kv_head + j) * d + k);
+                dp[j] = acc;
+                Di += acc * p[j];
+            }
+            if (a->D) a->D[r] = Di;
+            for (int64_t j = 0; j < j_end; ++j) {
+                const double ds = p[j] * (dp[j] - Di);
+                for (int64_t k = 0; k < d; ++k) {
+                    dq[k] += a->scale * ds * widen(a->K, a->dtype, (kv_head + j) * d + k);
+                    dK[j * d + k] += a->scale * ds * widen(a->Q, a->dtype, q_off + k);
+                    dV[j * d + k] += p[j] * widen(a->dO, a->dtype, q_off + k);
+                }
+            }
+        }
+    }
+}
+
+static void* bwd_worker(void* p) {
+    bwd_job* a = (bwd_job*)p;
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(2 * (a->N_k > 0 ? a->N_k : 1)));
+    if (!buf) return (void*)1;
+    for (;;) {
+        int64_t bg = __sync_fetch_and_add(&a->next, 1);
+        if (bg >= a->B * a->H_kv) break;
+        bwd_group(a, bg, buf, buf + a->N_k);
+    }
+    free(buf);
+    return 0;
+}
+
+int oracle_attention_bwd(const void* Q, const void* K, const void* V, const void* dO, int dtype, int64_t B,
+                         int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, int causal, double scale,
+                         double* dQ, double* dK, double* dV, double* D, int nthreads) {
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return -1;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_q <= 0 || N_k <= 0 || d <= 0 || H % H_kv) return -1;
+    if (dtype < 0 || dtype > 2) return -1;
+    bwd_job job = {Q, K, V, dO, dtype, B, H, H_kv, N_q, N_k, d, causal != 0, scale, dQ, dK, dV, D, 0};
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 512) nthreads = 512;
+    pthread_t th[512];
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], 0, bwd_worker, &job) != 0) break;
+        started = t;
+    }
+    void* rc0 = bwd_worker(&job);
+    int bad = rc0 != 0;
+    for (int t = 1; t <= started; ++t) {
+        void* rc;
+        pthread_join(th[t], &rc);
+        bad |= rc != 0;
+    }
+    return bad ? -2 : 0;
 }

@@ -343,7 +343,60 @@ def pin_lse_matches_state(orc):
         assert r["m"] == s.max()
 
 
+# --------------------------------------------------------------------------- backward (section 5.1)
+def _loss(orc, Q, K, V, dO, causal):
+    O, _ = orc.attention(Q, K, V, causal=causal, nthreads=1)
+    return float(np.sum(dO * O))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient equals the central difference of sum(dO * O) (fp64, h = 1e-5): with the
+    causal mask, a query longer than the keys (bottom-right alignment) and two query heads
+    sharing one key/value head.  Independent of the backward formulas: only the forward is used."""
+    rng = np.random.default_rng(7)
+    h = 1e-5
+    for causal, (N_q, N_k) in ((False, (4, 6)), (True, (5, 4)), (True, (3, 6))):
+        Q = rng.standard_normal((1, 2, N_q, 3))
+        K = rng.standard_normal((1, 1, N_k, 3))
+        V = rng.standard_normal((1, 1, N_k, 3))
+        dO = rng.standard_normal((1, 2, N_q, 3))
+        dQ, dK, dV, _ = orc.attention_bwd(Q, K, V, dO, causal=causal, nthreads=1)
+        for X, G in ((Q, dQ), (K, dK), (V, dV)):
+            num = np.empty_like(X)
+            for idx in np.ndindex(X.shape):
+                keep = X[idx]
+                X[idx] = keep + h
+                up = _loss(orc, Q, K, V, dO, causal)
+                X[idx] = keep - h
+                down = _loss(orc, Q, K, V, dO, causal)
+                X[idx] = keep
+                num[idx] = (up - down) / (2 * h)
+            assert np.max(np.abs(num - G)) <= 1e-7, (causal, N_q, N_k, np.max(np.abs(num - G)))
+
+
+def pin_bwd_d_identity(orc):
+    """Exercise 6 of Lecture 11: D_i = sum_j dP_ij P_ij equals dO_i . O_i."""
+    Q, K, V = _bf16_inputs(21, 2, 4, 2, 37, 29, 16)
+    dO = gen.normal_bf16(21, 3, (2, 4, 37, 16))
+    for causal in (False, True):
+        O, _ = orc.attention(Q, K, V, causal=causal)
+        _, _, _, D = orc.attention_bwd(Q, K, V, dO, causal=causal)
+        assert np.max(np.abs(D - np.sum(_f64(dO) * O, axis=-1))) <= 1e-12
+
+
+def pin_bwd_single_key(orc):
+    """One key: P = 1, so the scores do not matter (dQ = dK = 0) and dV is the sum of dO over
+    the group's query heads and rows."""
+    Q, K, V = _bf16_inputs(22, 2, 4, 2, 9, 1, 8)
+    dO = gen.normal_bf16(22, 3, (2, 4, 9, 8))
+    dQ, dK, dV, _ = orc.attention_bwd(Q, K, V, dO)
+    assert np.all(dQ == 0.0) and np.all(dK == 0.0)
+    want = _f64(dO).reshape(2, 2, 2, 9, 8).sum(axis=(2, 3))  # heads (g, within-group), rows
+    assert np.max(np.abs(dV[:, :, 0, :] - want)) <= 1e-12
+
+
 ALL_PINS = [pin_rows_sum_to_one, pin_single_key, pin_equal_scores, pin_causal_first_row,
             pin_fully_masked_rows, pin_large_scores, pin_torch_sdpa, pin_brute_force_decimal, pin_linearity_and_permutation,
             pin_gqa, pin_row_selection, pin_exercise1, pin_online_equals_full, pin_merge_orders,
-            pin_split_combine, pin_lse_matches_state]
+            pin_split_combine, pin_lse_matches_state, pin_bwd_finite_differences, pin_bwd_d_identity,
+            pin_bwd_single_key]

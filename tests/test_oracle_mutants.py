@@ -35,6 +35,16 @@ MUTANTS = [
     ("merge_max_is_min", "double m = m_a > m_b ? m_a : m_b;", "double m = m_a < m_b ? m_a : m_b;"),
     ("combine_weight_uses_max", "double w = exp(lse_s[t] - lse);", "double w = exp(lse_s[t] - M);"),
     ("combine_lse_without_max", "double lse = M + log(sum);", "double lse = log(sum);"),
+    ("bwd_drop_D", "const double ds = p[j] * (dp[j] - Di);", "const double ds = p[j] * dp[j];"),
+    ("bwd_dS_sign", "const double ds = p[j] * (dp[j] - Di);", "const double ds = p[j] * (Di - dp[j]);"),
+    ("bwd_dq_no_scale", "dq[k] += a->scale * ds *", "dq[k] += ds *"),
+    ("bwd_dk_uses_dO", "dK[j * d + k] += a->scale * ds * widen(a->Q, a->dtype, q_off + k);",
+     "dK[j * d + k] += a->scale * ds * widen(a->dO, a->dtype, q_off + k);"),
+    ("bwd_dv_uses_dS", "dV[j * d + k] += p[j] * widen(a->dO", "dV[j * d + k] += ds * widen(a->dO"),
+    ("bwd_dp_uses_K", "acc += widen(a->dO, a->dtype, q_off + k) * widen(a->V, a->dtype, (kv_head + j) * d + k);",
+     "acc += widen(a->dO, a->dtype, q_off + k) * widen(a->K, a->dtype, (kv_head + j) * d + k);"),
+    ("bwd_causal_ignored", "        if (a->causal) {\n                int64_t last = i + N_k - N_q;", "        if (0) {\n                int64_t last = i + N_k - N_q;"),
+    ("bwd_no_max_shift_unnormalised", "for (int64_t j = 0; j < j_end; ++j) p[j] /= l;", ""),
 ]
 
 
