@@ -7,6 +7,7 @@ gfx950 kernels; there is no CPU fallback.  PyTorch is used only to hold device
 memory and to name the stream.
 
     fwd(q, k, v, causal=False, scale=None)   -> (o, lse)          fa_fwd
+    bwd(q, k, v, o, lse, do, causal, scale)  -> (dq, dk, dv)      fa_bwd
     decode_split(q, k, v, num_splits, scale) -> (o_part, lse_part) fa_decode_split
     combine(o_part, lse_part)                -> (o, lse)          fa_combine
     decode(q, k, v, num_splits=None, scale)  -> (o, lse)          both, on one stream
@@ -17,7 +18,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "decode_split", "decode_split_paged", "combine", "decode", "decode_num_splits",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "decode_split", "decode_split_paged", "combine", "decode", "decode_num_splits",
            "decode_workspace_bytes",
            "fwd_tile_shape", "fwd_tile_count", "strerror", "library", "library_path", "FAError"]
 
@@ -48,6 +49,9 @@ def library():
         lib = ctypes.CDLL(LIBRARY)
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_decode_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
         lib.fa_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                               f32, vp]
@@ -60,7 +64,7 @@ def library():
         lib.fa_fwd_tile_count.restype = ctypes.c_longlong
         lib.fa_strerror.argtypes = [i32]
         lib.fa_strerror.restype = ctypes.c_char_p
-        for fn in (lib.fa_fwd, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits,
+        for fn in (lib.fa_fwd, lib.fa_bwd, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits,
                    lib.fa_fwd_tile_shape):
             fn.restype = i32
         _lib = lib
@@ -131,6 +135,47 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     _check("fa_fwd", library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                       B, H, H_kv, N_q, N_k, d, int(bool(causal)), float(scale), _stream_ptr(q)))
     return out, lse
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+        workspace=None):
+    """fa_bwd.  q, o, do [B,H,N_q,d], k/v [B,H_kv,N_k,d] bf16, lse [B,H,N_q] fp32 (the forward's)
+    -> dq [B,H,N_q,d], dk/dv [B,H_kv,N_k,d] bf16.  workspace: fp32 tensor of at least B*H*N_q
+    elements (allocated when None)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, H, N_q, d = q.shape
+    Bk, H_kv, N_k, dk_ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk_ != d:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, N_q):
+        raise ValueError("o, do and lse must match q: o %s do %s lse %s" % (tuple(o.shape), tuple(do.shape),
+                                                                           tuple(lse.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _need(t, n, torch.bfloat16, 4)
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError("%s must have shape %s" % (n, tuple(ref.shape)))
+    if workspace is None:
+        workspace = torch.empty(B * H * N_q, dtype=torch.float32, device=q.device)
+    _need(workspace, "workspace", torch.float32, 1)
+    if workspace.numel() * 4 < bwd_workspace_bytes(B, H, N_q):
+        raise ValueError("workspace too small: %d floats, need %d" % (workspace.numel(), B * H * N_q))
+    _check("fa_bwd", library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                      workspace.data_ptr(), B, H, H_kv, N_q, N_k, d, int(bool(causal)),
+                                      float(scale), _stream_ptr(q)))
+    return dq, dk, dv
+
+
+def bwd_workspace_bytes(B: int, H: int, N_q: int) -> int:
+    return int(library().fa_bwd_workspace_bytes(B, H, N_q))
 
 
 def decode_split(q, k, v, num_splits: int, scale: float | None = None, o_part=None, lse_part=None):

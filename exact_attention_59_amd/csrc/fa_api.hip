@@ -109,6 +109,36 @@ FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float
                   "fa_fwd");
 }
 
+FA_EXPORT int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                     void* dQ, void* dK, void* dV, float* workspace, int B, int H, int H_kv, int N_q, int N_k, int d,
+                     int causal, float scale, void* stream) {
+    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !workspace) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_q <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
+    if (H % H_kv) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * N_q * d >= kMaxElems || (long long)B * H_kv * N_k * d >= kMaxElems)
+        return FA_ERR_UNSUPPORTED;
+    const long long q_blocks = (long long)((N_q + fa::kBwdBlockRows - 1) / fa::kBwdBlockRows) * B * H;
+    const long long k_blocks = (long long)((N_k + fa::kBwdBlockKeys - 1) / fa::kBwdBlockKeys) * B * H_kv;
+    if (q_blocks > 0x7fffffffLL || k_blocks > 0x7fffffffLL || (long long)B * H * N_q / 16 > 0x7fffffffLL)
+        return FA_ERR_UNSUPPORTED;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(dO) || misaligned(LSE) ||
+        misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(workspace))
+        return FA_ERR_ALIGN;
+    if (!isfinite(scale)) return FA_ERR_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] bwd B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d causal=%d\n", B, H, H_kv, N_q, N_k, d, causal);
+    return finish(fa::launch_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B, H, H_kv, N_q, N_k, d, causal == 1,
+                                 scale, static_cast<hipStream_t>(stream)),
+                  "fa_bwd");
+}
+
+FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int H, int N_q) {
+    if (B <= 0 || H <= 0 || N_q <= 0) return 0;
+    return (size_t)B * H * N_q * sizeof(float);
+}
+
 FA_EXPORT int fa_decode_split(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
                               int B, int H, int H_kv, int N_k, int d, int num_splits, float scale,
                               void* stream) {

@@ -98,4 +98,22 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// Copy 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at LDS byte address lds_base + 16 * l.  Issued as inline assembly so
+// that the compiler's wait-count bookkeeping does not see it: the compiler counts such a
+// copy as both a vector-memory and an LDS access, which would turn every LDS-read wait in
+// the loop into a full wait.  Completion is awaited explicitly with wait_vmem(), and the
+// workgroup barrier after that orders it before any read of the buffer.
+__device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+
+// s_waitcnt vmcnt(0): this wave's global->LDS copies have landed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
 }  // namespace fa

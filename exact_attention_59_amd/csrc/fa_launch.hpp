@@ -12,12 +12,24 @@ namespace fa {
 constexpr int kFwdBlockRows = 128;
 constexpr int fwd_block_cols(int /*d*/) { return 64; }
 
+// Backward tile shapes: the dQ kernel's query rows per workgroup and keys per tile; the
+// dK/dV kernel's keys per workgroup and queries per tile.
+constexpr int kBwdBlockRows = 128;
+constexpr int bwd_dq_block_cols(int d) { return d == 128 ? 32 : 64; }
+constexpr int kBwdBlockKeys = 128;
+constexpr int kBwdBlockQueries = 32;
+
 // Decode: keys per wave iteration and query heads per workgroup.
 constexpr int kDecKeysPerWave = 32;
 constexpr int kDecHeadsPerBlock = 16;
 
 hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
                       int H_kv, int N_q, int N_k, int d, bool causal, float scale, hipStream_t stream);
+
+// Backward: D = rowsum(dO * O) into `workspace` (B*H*N_q floats), then dQ, then dK and dV.
+hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+                      void* dQ, void* dK, void* dV, float* workspace, int B, int H, int H_kv, int N_q, int N_k, int d,
+                      bool causal, float scale, hipStream_t stream);
 
 hipError_t launch_decode_split(const void* Q, const void* K, const void* V, float* O_part,
                                float* LSE_part, int B, int H, int H_kv, int N_k, int d, int num_splits,

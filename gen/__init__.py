@@ -6,7 +6,8 @@ Box-Muller pair per two words, float rounding, a float multiply by ``scale``
 and (for bf16) round-to-nearest-even.  Every element is addressable by
 (seed, tensor id, linear index), so any slice can be regenerated on its own.
 
-Tensor ids used by the tests and the bench: Q = 0, K = 1, V = 2.
+Tensor ids used by the tests and the bench: Q = 0, K = 1, V = 2, dO (the upstream
+gradient of the backward pass) = 3.
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ _SRC = os.path.join(_HERE, "gen.c")
 _LIB = os.path.join(_HERE, "libgen.so")
 _lib = None
 
-TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DO = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:

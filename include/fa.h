@@ -1,10 +1,12 @@
 /*
  * fa.h -- C ABI of libfa.so: exact attention on AMD Instinct MI355X (gfx950).
  *
- * Three compute entry points:
+ * Compute entry points:
  *   fa_fwd           FlashAttention-2 forward: O = softmax(scale * Q K^T) V and the
  *                    per-row log-sum-exp, computed tile by tile with the online
  *                    softmax state (m, l, acc); S and P never reach device memory.
+ *   fa_bwd           FlashAttention backward: dQ, dK, dV from dO, recomputing P on
+ *                    chip from the saved log-sum-exp.
  *   fa_decode_split  flash-decoding, step 2: one query token per sequence, keys cut
  *                    into num_splits contiguous segments, per-segment normalised
  *                    output o_s and lse_s.
@@ -72,6 +74,34 @@ typedef enum {
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
            int N_q, int N_k, int d, int causal, float scale, void* stream);
+
+/*
+ * Exact attention backward (Lecture 11 section 5.1): for the forward above with the
+ * same Q, K, V, causal and scale, and the upstream gradient dO, computes
+ *   D_i = dO_i . O_i,  P_ij = exp(scale * q_i . k_j - LSE_i) over the visible keys,
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ * P is recomputed from LSE (section 5.1's one-exp recovery); S, P and dS never reach
+ * device memory.  With grouped heads, dK and dV of key/value head g sum over the query
+ * heads that read it.  Every gradient row is written by exactly one workgroup: no
+ * atomics, and the result is the same on every call.
+ *   Q, K, V, causal, scale  as for fa_fwd
+ *   O   [B][H][N_q][d]    bf16, read (the forward's output)
+ *   dO  [B][H][N_q][d]    bf16, read
+ *   LSE [B][H][N_q]       fp32, read (the forward's; -inf marks a row with no visible key)
+ *   dQ  [B][H][N_q][d]    bf16, written
+ *   dK  [B][H_kv][N_k][d] bf16, written (zero for a key no query sees)
+ *   dV  [B][H_kv][N_k][d] bf16, written
+ *   workspace  fa_bwd_workspace_bytes(B, H, N_q) bytes of device memory, 16-byte
+ *              aligned, owned by the caller; it receives D (fp32) and may be reused
+ *              once the call's work on `stream` has finished.
+ * Limits: as for fa_fwd.  The three kernels run in order on `stream`.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
+           void* dQ, void* dK, void* dV, float* workspace, int B, int H, int H_kv, int N_q, int N_k, int d,
+           int causal, float scale, void* stream);
+
+/* Bytes of workspace fa_bwd needs: 4 * B * H * N_q (0 if a size is <= 0). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N_q);
 
 /*
  * Flash-decoding split step (Lecture 11 section 6.2, steps 1-2): one query token

@@ -4,6 +4,18 @@ Gates (GPU result vs the fp64 oracle on the same bf16 inputs):
   O:   max |err| <= 2e-2 and mean |err| <= 2e-3 (bf16 output, fp32 accumulation)
   LSE: max |err| <= 1e-3
   every output finite where the oracle is finite; -inf LSE / zero O where no key is visible.
+
+Gradient gates (dQ, dK, dV of the backward; each tensor on its own), normwise with
+u = 2^-9, the unit roundoff of bf16 (m = max(max |ref|, 1e-2), a = max(mean |ref|, 1e-2);
+the floor only matters for all-zero gradients):
+  max |err| <= 4u m = 2^-7 m   and   mean |err| <= 2u a = 2^-8 a.
+Derivation: every gradient element is rounded to bf16 once at the end (error at most
+u |x|, about u |x| / 2 on average), and one factor of each product (P for dV, dS for dQ
+and dK) is rounded to bf16 before it (at most u per term; the terms' signs are random, so
+the sum's error stays of the order of u times the element's own size).  Both together
+put the largest error near 2u of the largest element and the mean near u of the mean
+element; an fp64 emulation of exactly these rounding points reproduces the kernel's
+error statistics.  The gates allow twice that.
 """
 from __future__ import annotations
 
@@ -15,6 +27,7 @@ import numpy as np
 import gen
 
 O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+G_MAX, G_MEAN, G_FLOOR = 2.0 ** -7, 2.0 ** -8, 1e-2
 
 
 def say(*args):
@@ -87,6 +100,25 @@ def check(name, O_gpu, O_ref, L_gpu, L_ref):
     assert res["o_mean"] <= O_MEAN, "%s: O mean-abs %.3g > %.3g" % (name, res["o_mean"], O_MEAN)
     assert res["lse_max"] <= LSE_MAX, "%s: LSE max-abs %.3g > %.3g" % (name, res["lse_max"], LSE_MAX)
     return res
+
+
+def check_grads(name, gpu, ref):
+    """Apply the gradient gates to (dQ, dK, dV); returns the errors relative to m and a."""
+    out = {}
+    for label, g, r in zip(("dQ", "dK", "dV"), gpu, ref):
+        g = np.asarray(g, dtype=np.float64)
+        r = np.asarray(r, dtype=np.float64)
+        assert g.shape == r.shape, "%s %s: shape %s vs %s" % (name, label, g.shape, r.shape)
+        assert np.all(np.isfinite(g)), "%s: non-finite %s" % (name, label)
+        m = max(float(np.abs(r).max()), G_FLOOR)
+        a = max(float(np.abs(r).mean()), G_FLOOR)
+        err = np.abs(g - r)
+        out[label] = (float(err.max()) / m, float(err.mean()) / a, m)
+    say(name, {k: "max %.2e m, mean %.2e a (m %.3g)" % v for k, v in out.items()})
+    for label, (mx, mn, _) in out.items():
+        assert mx <= G_MAX, "%s: %s max-abs %.3g m > %.3g m" % (name, label, mx, G_MAX)
+        assert mn <= G_MEAN, "%s: %s mean-abs %.3g a > %.3g a" % (name, label, mn, G_MEAN)
+    return out
 
 
 def gpu_available():

@@ -37,7 +37,7 @@ def exported_symbols(path):
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_decode_split", "fa_decode_split_paged", "fa_combine", "fa_decode_num_splits",
+    for want in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_split", "fa_decode_split_paged", "fa_combine", "fa_decode_num_splits",
                  "fa_decode_workspace_bytes", "fa_strerror", "fa_fwd_tile_shape", "fa_fwd_tile_count"):
         assert want in names
 
@@ -59,6 +59,31 @@ P_MIS = ctypes.c_void_p(0x100004)   # 4-byte aligned only
 
 def fwd(lib, Q=P, K=P, V=P, O=P, L=P, B=1, H=1, H_kv=1, N_q=8, N_k=8, d=64, causal=0, scale=0.125):
     return lib.fa_fwd(Q, K, V, O, L, B, H, H_kv, N_q, N_k, d, causal, scale, None)
+
+
+def bwd(lib, Q=P, K=P, V=P, O=P, dO=P, L=P, dQ=P, dK=P, dV=P, W=P, B=1, H=2, H_kv=1, N_q=8, N_k=8, d=64, causal=0,
+        scale=0.125):
+    return lib.fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, W, B, H, H_kv, N_q, N_k, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(O=None), fa.FA_ERR_NULL), (dict(dO=None), fa.FA_ERR_NULL),
+    (dict(L=None), fa.FA_ERR_NULL), (dict(dQ=None), fa.FA_ERR_NULL), (dict(dK=None), fa.FA_ERR_NULL),
+    (dict(dV=None), fa.FA_ERR_NULL), (dict(W=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(N_q=0), fa.FA_ERR_SHAPE), (dict(N_k=-1), fa.FA_ERR_SHAPE),
+    (dict(H=3, H_kv=2), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dO=P_MIS), fa.FA_ERR_ALIGN), (dict(dK=P_MIS), fa.FA_ERR_ALIGN), (dict(W=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(scale=float("inf")), fa.FA_ERR_ARG), (dict(causal=3), fa.FA_ERR_ARG),
+])
+def test_bwd_validation(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_bytes(lib):
+    assert fa.bwd_workspace_bytes(2, 16, 1000) == 2 * 16 * 1000 * 4
+    assert fa.bwd_workspace_bytes(0, 16, 1000) == 0
+    assert fa.bwd_workspace_bytes(1, 1, -3) == 0
 
 
 def dec(lib, Q=P, K=P, V=P, Op=P, Lp=P, B=1, H=4, H_kv=1, N_k=64, d=128, S=4, scale=0.1):
