@@ -9,7 +9,9 @@ FLOPs (4*B*H*N_q*N_k*d, halved under the causal mask) over its GPU time, in TFLO
 The flash-decoding leg (B=4, H=32, H_kv=8, d=128, N_k = 4096 and 65536; split kernel
 then combine kernel) runs in the same invocation and is reported under "decode" in
 GB/s of K+V read once, against the 8 TB/s HBM peak; a 640 MB read sweep before every
-timed decode repetition evicts K/V from the 256 MB last-level cache.
+timed decode repetition evicts K/V from the 256 MB last-level cache.  The backward leg
+(fa_bwd on the same prefill shape) is reported under "backward", in TFLOP/s of its five
+N_q x N_k x d products.
 
 Inputs are synthetic and seeded (counter-based SplitMix64 + Box-Muller, see gen/),
 already resident in device memory when timing starts.  GPU times come from HIP
@@ -154,6 +156,53 @@ def leg_forward_other(fa, torch, reps, name, seed, B, H, H_kv, N, d, causal):
             "pct_peak": 100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bwd_flops(B, H, N_q, N_k, d, causal):
+    """Five N_q x N_k x d products (S recomputed, dV, dP, dQ, dK), halved under the causal mask."""
+    return 5.0 * 2.0 * B * H * N_q * N_k * d / (2.0 if causal else 1.0)
+
+
+def leg_backward(fa, torch, reps, B=16, H=16, H_kv=16, N=1024, seed=2):
+    """fa_bwd (D pre-pass, dQ kernel, dK/dV kernel) on the batched-prefill shape, O and LSE
+    from fa_fwd on the same inputs; d = 64 with and without the causal mask, d = 128 without."""
+    import gen
+
+    res = {}
+    for d, causal in ((64, False), (64, True), (128, False)):
+        Q, K, V = fwd_inputs(seed, B, H, H_kv, N, d)
+        q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
+        do = dev_bf16(gen.normal_bf16(seed, gen.TENSOR_DO, (B, H, N, d)))
+        o, lse = fa.fwd(q, k, v, causal=causal)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(B * H * N, dtype=torch.float32, device="cuda")
+        call = lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record(torch.cuda.current_stream())
+        while True:  # >= 30 ms of GPU time first, past the clock dip
+            for _ in range(5):
+                call()
+            w1.record(torch.cuda.current_stream())
+            w1.synchronize()
+            if w0.elapsed_time(w1) >= 30.0:
+                break
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        stream = torch.cuda.current_stream()
+        ev[0].record(stream)
+        for i in range(reps):
+            call()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+        ms = sum(times) / reps
+        fl = bwd_flops(B, H, N, N, d, causal)
+        res["d=%d %s" % (d, "causal" if causal else "non-causal")] = {
+            "us": round(ms * 1e3, 2), "us_min": round(times[0] * 1e3, 2),
+            "tflops_5_products": round(fl / (ms * 1e-3) / 1e12, 1),
+            "pct_bf16_peak": round(100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+    return {"workload": "backward B=16 H=16 N_q=N_k=1024 bf16 (dO seeded N(0,1))", "flops_convention":
+            "5 * 2*B*H*N_q*N_k*d, halved under the causal mask (the backward's five products)", "runs": res}
+
+
 def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=None):
     import gen
 
@@ -289,7 +338,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
-    ap.add_argument("--legs", default="fwd,decode,cpu", help="comma list of fwd, decode, cpu, copy")
+    ap.add_argument("--legs", default="fwd,decode,bwd,cpu", help="comma list of fwd, decode, bwd, cpu, copy")
     ap.add_argument("--all", action="store_true", help="also time the long-sequence and GQA forward workloads")
     ap.add_argument("--decode-reps", type=int, default=30)
     ap.add_argument("--decode-nk", default="4096,65536", help="comma list of decode cache lengths")
@@ -355,6 +404,12 @@ def main():
             log("decode", dec["N_k=%d" % N_k])
             torch.cuda.empty_cache()
         out["decode"] = dec
+
+    if "bwd" in legs:
+        log("backward leg")
+        out["backward"] = leg_backward(fa, torch, 30)
+        log("backward", out["backward"])
+        torch.cuda.empty_cache()
 
     if args.all:
         others = [("long causal B=2 H=16 N=8192 d=128", 3, 2, 16, 16, 8192, 128, True),

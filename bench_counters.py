@@ -33,7 +33,8 @@ COPY_BYTES = 1024 ** 3  # bench.py leg_copy: 1 GiB read and 1 GiB written per co
 
 
 def kernel_key(name: str) -> str | None:
-    m = re.search(r"(fwd_kernel<\d+, (?:true|false)>|decode_split_kernel<\d+>|combine_kernel<\d+>)", name)
+    m = re.search(r"(fwd_kernel<\d+, (?:true|false)>|decode_split_kernel<\d+(?:, (?:true|false))?>|combine_kernel<\d+>)",
+                  name)
     if m:
         return m.group(1)
     if "copy" in name.lower() and "fill" not in name.lower():
@@ -53,10 +54,10 @@ def read_counter(run_dir: str, counter: str, label: str = "", per=None) -> dict:
                 continue
             key = kernel_key(row["Kernel_Name"])
             if key:
-                if key != "copy":
-                    key += " grid=%s" % row["Grid_Size"]
-                    if label and not key.startswith("fwd_kernel"):
-                        key += " " + label
+                key += " grid=%s" % row["Grid_Size"]
+                # the prefill launches are the same in every run; the rest depend on N_k
+                if label and not key.startswith(("copy", "fwd_kernel<64")):
+                    key += " " + label
                 per[key][(f, row["Dispatch_Id"])] += float(row["Counter_Value"])
     return per
 
@@ -84,13 +85,18 @@ def main():
         fetch_per = read_counter(f_dir, "FETCH_SIZE", label, fetch_per)
         write_per = read_counter(w_dir, "WRITE_SIZE", label, write_per)
     fetch, write = averages(fetch_per), averages(write_per)
-    if "copy" not in fetch or "copy" not in write:
+    # The calibration copy is the 1 GiB one: the largest copy dispatch (other, small
+    # runtime copies of the bench's set-up also match the name).
+    copies = [k for k in fetch if k.startswith("copy") and k in write]
+    if not copies:
         raise SystemExit("the copy kernel is missing from the runs (use --legs ...,copy)")
+    big = max(copies, key=lambda k: fetch[k])
+    fetch["copy"], write["copy"] = fetch[big], write[big]
     f_read = COPY_BYTES / (fetch["copy"] * 1024.0)
     f_write = COPY_BYTES / (write["copy"] * 1024.0)
     kernels = {}
     for k in sorted(set(fetch) & set(write)):
-        if k == "copy":
+        if k.startswith("copy"):
             continue
         kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
                       "hbm_read_bytes_per_launch": round(fetch[k] * 1024 * f_read),
