@@ -79,6 +79,15 @@ class Oracle:
         lib.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, i32, d64,
                                              vp, vp, vp, vp, i32]
         lib.oracle_attention_bwd.restype = i32
+        u64, f32 = ctypes.c_uint64, ctypes.c_float
+        lib.oracle_fp8_quantize.argtypes = [vp, i64, i64, i64, i64, i32, u64, u64, f32, vp, vp]
+        lib.oracle_fp8_quantize.restype = i32
+        lib.oracle_e4m3_encode_n.argtypes = [vp, i64, vp]
+        lib.oracle_e4m3_encode_n.restype = None
+        lib.oracle_e4m3_decode_n.argtypes = [vp, i64, vp]
+        lib.oracle_e4m3_decode_n.restype = None
+        lib.oracle_fwht_rows.argtypes = [vp, i64, i64]
+        lib.oracle_fwht_rows.restype = None
         self.lib = lib
 
     # ------------------------------------------------------------------ Algorithm 0
@@ -190,6 +199,46 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_attention_bwd failed with code %d" % rc)
         return dQ, dK, dV, D
+
+
+    # ------------------------------------------------------------------ FP8 quantisation
+    def e4m3_encode(self, x):
+        """float32 array -> uint8 OCP e4m3fn codes (nearest-even)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint8)
+        self.lib.oracle_e4m3_encode_n(x.ctypes.data, x.size, out.ctypes.data)
+        return out
+
+    def e4m3_decode(self, c):
+        """uint8 e4m3fn codes -> float64 values (NaN for the NaN codes)."""
+        c = np.ascontiguousarray(c, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_e4m3_decode_n(c.ctypes.data, c.size, out.ctypes.data)
+        return out
+
+    def fwht(self, x):
+        """fp32 fast Walsh-Hadamard transform (unnormalised) of every row of x [..., d]."""
+        x = np.array(x, dtype=np.float32, copy=True, order="C")
+        d = x.shape[-1]
+        self.lib.oracle_fwht_rows(x.ctypes.data, x.size // d, d)
+        return x
+
+    def fp8_quantize(self, X, block, transform=False, sign_lo=0, sign_hi=0, post_scale=1.0):
+        """bf16 X [..., N, d] (uint16 bits) -> (codes uint8 [..., N, d], scales float32 [..., ceil(N/block)])."""
+        X = np.ascontiguousarray(X)
+        if X.dtype != np.uint16:
+            raise TypeError("X must hold bf16 bits (uint16)")
+        *lead, N, d = X.shape
+        n_heads = int(np.prod(lead)) if lead else 1
+        n_blocks = -(-N // block)
+        codes = np.empty(X.shape, dtype=np.uint8)
+        scales = np.empty(tuple(lead) + (n_blocks,), dtype=np.float32)
+        rc = self.lib.oracle_fp8_quantize(X.ctypes.data, n_heads, N, d, block, int(bool(transform)),
+                                          int(sign_lo) & (2**64 - 1), int(sign_hi) & (2**64 - 1),
+                                          float(post_scale), codes.ctypes.data, scales.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_fp8_quantize failed with code %d" % rc)
+        return codes, scales
 
 
 _default = None

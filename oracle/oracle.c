@@ -29,6 +29,10 @@
  *                      sum(dO * O) with respect to Q, K, V from the full
  *                      probability matrix P (the "standard" backward that the
  *                      section compares FlashAttention's against).
+ *   oracle_fp8_quantize the FP8 path's input quantisation (block scales after a
+ *                      random-sign Hadamard transform; the FlashAttention v3
+ *                      card of the course page), with its e4m3 encoder and
+ *                      the fast Walsh-Hadamard transform; fp32, see its notes.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - layout: Q [B][H][N_q][d], K and V [B][H_kv][N_k][d], row-major;
@@ -407,4 +411,117 @@ int oracle_attention_bwd(const void* Q, const void* K, const void* V, const void
         bad |= rc != 0;
     }
     return bad ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * FP8 (e4m3) block quantisation with incoherent processing -- the input side of an FP8
+ * attention forward (FlashAttention v3 card of the course page, "FP8 path"; Lecture 11
+ * section 4.4's list): one scale per block of rows, and before quantising, multiply the
+ * rows by a random orthogonal matrix so that an outlier channel is spread over all
+ * channels.  The pages fix nothing further; the readings taken here:
+ *   - format: OCP e4m3fn (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+ *     finite 448, subnormals down to 2^-9, code 0x7F / 0xFF is NaN), rounding to nearest,
+ *     ties to even;
+ *   - transform: x -> (s o x) H, with s a vector of d random signs (bit j of the 128-bit
+ *     mask (hi:lo) set means -1) and H the unnormalised Sylvester-Hadamard matrix, applied
+ *     by the fast transform whose stage len = 1, 2, 4, ..., d/2 replaces every pair
+ *     (x_i, x_{i+len}) with i & len == 0 by (x_i + x_{i+len}, x_i - x_{i+len}).  Since
+ *     H H^T = d I, scores of transformed rows are d times the original ones;
+ *   - per block of `block` consecutive rows of one head: amax = max |x| over the block,
+ *     r = 448 / amax, code = e4m3(x * r), stored scale = (amax / 448) * post_scale
+ *     (post_scale = 1/d for transformed queries, so that dequantised q . k equals the
+ *     original score; 1 otherwise); an all-zero block gets r = 0 and scale 0;
+ *   - arithmetic: fp32, in exactly the order written (the code is an integer decided by
+ *     floating point, and the kernel decides it in fp32).
+ * --------------------------------------------------------------------------------------- */
+
+/* Round a float to OCP e4m3fn, nearest-even; beyond the largest finite value's rounding
+ * range (|x| > 464) or NaN gives the NaN code. */
+uint8_t oracle_e4m3_encode(float x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs((double)x);
+    if (isnan(x) || a > 464.0) return (uint8_t)(sign | 0x7F);
+    if (a < ldexp(1.0, -6)) {                      /* subnormal range: units of 2^-9 */
+        double q = nearbyint(ldexp(a, 9));        /* 0..8; 8 is the smallest normal */
+        return (uint8_t)(sign | (uint8_t)q);
+    }
+    int e;
+    (void)frexp(a, &e);                            /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;                                        /* a = (1 + m) * 2^e */
+    double m8 = nearbyint(ldexp(a, 3 - e)) - 8.0;  /* mantissa in eighths, 0..8 */
+    if (m8 >= 8.0) {
+        m8 = 0.0;
+        e += 1;
+    }
+    if (e + 7 > 15 || (e + 7 == 15 && m8 >= 7.0)) return (uint8_t)(sign | 0x7F);
+    return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)m8);
+}
+
+double oracle_e4m3_decode(uint8_t c) {
+    const double s = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return s * ldexp((double)m, -9);
+    return s * ldexp(8.0 + m, e - 10);
+}
+
+/* In-place fast Walsh-Hadamard transform of one row (fp32, the stage order above). */
+void oracle_fwht_f32(float* x, int64_t d) {
+    for (int64_t len = 1; len < d; len <<= 1)
+        for (int64_t i = 0; i < d; ++i)
+            if ((i & len) == 0) {
+                const float a = x[i], b = x[i + len];
+                x[i] = a + b;
+                x[i + len] = a - b;
+            }
+}
+
+/* X: bf16 [n_heads][N][d].  codes: [n_heads][N][d] e4m3; scales: [n_heads][ceil(N/block)].
+ * Returns 0, or -1 for invalid sizes (d not a power of two when transform is set). */
+int oracle_fp8_quantize(const uint16_t* X, int64_t n_heads, int64_t N, int64_t d, int64_t block, int transform,
+                        uint64_t sign_lo, uint64_t sign_hi, float post_scale, uint8_t* codes, float* scales) {
+    if (n_heads <= 0 || N <= 0 || d <= 0 || block <= 0 || d > 128) return -1;
+    if (transform && (d & (d - 1))) return -1;
+    const int64_t n_blocks = (N + block - 1) / block;
+    float* buf = (float*)malloc(sizeof(float) * (size_t)(block * d));
+    if (!buf) return -1;
+    for (int64_t h = 0; h < n_heads; ++h)
+        for (int64_t t = 0; t < n_blocks; ++t) {
+            const int64_t r0 = t * block, r1 = (r0 + block < N) ? r0 + block : N;
+            float amax = 0.0f;
+            for (int64_t r = r0; r < r1; ++r) {
+                float* x = buf + (r - r0) * d;
+                for (int64_t j = 0; j < d; ++j) {
+                    uint32_t bits = (uint32_t)X[(h * N + r) * d + j] << 16;
+                    memcpy(&x[j], &bits, 4);
+                    if (transform) {
+                        const int neg = j < 64 ? (int)((sign_lo >> j) & 1u) : (int)((sign_hi >> (j - 64)) & 1u);
+                        if (neg) x[j] = -x[j];
+                    }
+                }
+                if (transform) oracle_fwht_f32(x, d);
+                for (int64_t j = 0; j < d; ++j)
+                    if (fabsf(x[j]) > amax) amax = fabsf(x[j]);
+            }
+            const float rcp = amax > 0.0f ? 448.0f / amax : 0.0f;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t j = 0; j < d; ++j) {
+                    const float y = buf[(r - r0) * d + j] * rcp;
+                    codes[(h * N + r) * d + j] = oracle_e4m3_encode(y);
+                }
+            scales[h * n_blocks + t] = amax > 0.0f ? (amax / 448.0f) * post_scale : 0.0f;
+        }
+    free(buf);
+    return 0;
+}
+
+/* Array forms for the Python front end. */
+void oracle_e4m3_encode_n(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+}
+void oracle_e4m3_decode_n(const uint8_t* c, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+void oracle_fwht_rows(float* x, int64_t rows, int64_t d) {
+    for (int64_t r = 0; r < rows; ++r) oracle_fwht_f32(x + r * d, d);
 }

@@ -395,8 +395,133 @@ def pin_bwd_single_key(orc):
     assert np.max(np.abs(dV[:, :, 0, :] - want)) <= 1e-12
 
 
+# ---------------------------------------------------------------------------------- FP8 quantisation
+def _torch_e4m3(x):
+    """Independent encoder: torch's float32 -> float8_e4m3fn conversion (nearest-even)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def pin_e4m3_codec(orc):
+    """The e4m3 encoder and decoder against torch's float8_e4m3fn: every code decodes to the
+    same value and re-encodes to itself; midpoints between neighbours round to the even code;
+    random values over the whole range (overflow beyond 464 included) encode identically."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    dec = orc.e4m3_decode(codes)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(dec), nan) and np.array_equal(dec[~nan], want[~nan])
+    finite = dec[~nan].astype(np.float32)
+    assert np.array_equal(orc.e4m3_encode(finite), _torch_e4m3(finite))
+    pos = np.unique(dec[(~nan) & (dec >= 0)])
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)  # exact halfway points (ties)
+    mids = np.concatenate([mids, -mids, mids * np.float32(1 + 2 ** -20), mids * np.float32(1 - 2 ** -20)])
+    assert np.array_equal(orc.e4m3_encode(mids), _torch_e4m3(mids))
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.uniform(-520, 520, 4000), rng.standard_normal(4000) * 2.0 ** rng.integers(-12, 9, 4000)])
+    x = x.astype(np.float32)
+    assert np.array_equal(orc.e4m3_encode(x), _torch_e4m3(x))
+
+
+def _hadamard(d):
+    from scipy.linalg import hadamard
+
+    return hadamard(d).astype(np.int64)
+
+
+def pin_fwht_exact(orc):
+    """On integer rows the fp32 transform is exact and equals x @ H (scipy's Sylvester
+    Hadamard matrix); applying it twice gives d * x (H H^T = d I)."""
+    rng = np.random.default_rng(41)
+    for d in (2, 8, 64, 128):
+        x = rng.integers(-100, 101, size=(5, d))
+        y = orc.fwht(x.astype(np.float32))
+        assert np.array_equal(y.astype(np.int64), x @ _hadamard(d))
+        assert np.array_equal(orc.fwht(y).astype(np.int64), d * x)
+
+
+def _bf16_ints(rng, shape, lo=-8, hi=9):
+    """Small integers as bf16 bits (exact)."""
+    v = rng.integers(lo, hi, size=shape).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16), v.astype(np.int64)
+
+
+def pin_fp8_quantize_composition(orc):
+    """Integer inputs, so the transform is exact: codes and scales equal the composition of
+    independent pieces -- the random signs, scipy's Hadamard matrix, the block max, numpy
+    float32 arithmetic for r = 448 / amax and x * r, torch's e4m3 encoder -- with the mask's
+    high word acting on channels 64..127 and a ragged last block."""
+    rng = np.random.default_rng(42)
+    d, N, block = 128, 150, 64
+    Xb, Xi = _bf16_ints(rng, (2, N, d))
+    lo, hi = 0x9E3779B97F4A7C15, 0x0123456789ABCDEF
+    signs = np.array([-1 if ((lo >> j) & 1 if j < 64 else (hi >> (j - 64)) & 1) else 1 for j in range(d)])
+    for transform, post in ((True, 1.0 / d), (False, 1.0)):
+        codes, scales = orc.fp8_quantize(Xb, block, transform, lo, hi, post)
+        Y = (Xi * signs) @ _hadamard(d) if transform else Xi
+        for h in range(2):
+            for t in range(-(-N // block)):
+                blk = Y[h, t * block:(t + 1) * block].astype(np.float32)  # exact (|y| < 2^24)
+                amax = np.float32(np.abs(blk).max())
+                r = np.float32(448.0) / amax
+                assert np.array_equal(codes[h, t * block:(t + 1) * block], _torch_e4m3(blk * r))
+                assert scales[h, t] == np.float32(amax / np.float32(448.0)) * np.float32(post)
+
+
+def pin_fp8_block_edges(orc):
+    """A block's largest element encodes to +-448 exactly; an all-zero block gives zero codes
+    and scale 0; blocks are independent (quantising two blocks together equals quantising each)."""
+    rng = np.random.default_rng(43)
+    Xb = gen.normal_bf16(43, 0, (1, 96, 64))
+    Xb[0, 32:64] = 0  # second block of 32 rows all zero
+    codes, scales = orc.fp8_quantize(Xb, 32, True, 0x1234, 0, 1.0 / 64)
+    assert np.all(codes[0, 32:64] == 0) and scales[0, 1] == 0.0
+    for t in (0, 2):
+        blk = codes[0, 32 * t:32 * t + 32]
+        assert np.sum((blk & 0x7F) == 0x7E) >= 1 and np.all((blk & 0x7F) <= 0x7E)
+    c0, s0 = orc.fp8_quantize(Xb[:, :32], 32, True, 0x1234, 0, 1.0 / 64)
+    c2, s2 = orc.fp8_quantize(Xb[:, 64:], 32, True, 0x1234, 0, 1.0 / 64)
+    assert np.array_equal(c0, codes[:, :32]) and np.array_equal(c2, codes[:, 64:])
+    assert s0[0, 0] == scales[0, 0] and s2[0, 0] == scales[0, 2]
+    del rng
+
+
+def pin_fp8_scores_preserved(orc):
+    """Dequantised transformed queries and keys reproduce the original scores q . k: the
+    orthogonal transform cancels (H H^T = d I, the 1/d carried by the query scales), and the
+    error stays within the bound that e4m3 rounding (at most 2^-4 relative, or half a
+    subnormal step) of each factor allows."""
+    B, H, N, d = 1, 2, 64, 128
+    Q = gen.normal_bf16(44, 0, (B, H, N, d))
+    K = gen.normal_bf16(44, 1, (B, H, N, d))
+    lo, hi = 0xF0F0F0F0A5A5A5A5, 0x0F0F0F0F5A5A5A5A
+    cq, sq = orc.fp8_quantize(Q, 32, True, lo, hi, 1.0 / d)
+    ck, sk = orc.fp8_quantize(K, 32, True, lo, hi, 1.0)
+    qd = orc.e4m3_decode(cq) * np.repeat(sq.astype(np.float64), 32, axis=-1)[..., None]
+    kd = orc.e4m3_decode(ck) * np.repeat(sk.astype(np.float64), 32, axis=-1)[..., None]
+    signs = np.array([-1.0 if ((lo >> j) & 1 if j < 64 else (hi >> (j - 64)) & 1) else 1.0 for j in range(d)])
+    Hm = _hadamard(d).astype(np.float64)
+    qt, kt = (_f64(Q) * signs) @ Hm / d, (_f64(K) * signs) @ Hm  # exact transformed rows
+    s_true = _f64(Q) @ np.swapaxes(_f64(K), -1, -2)
+    s_deq = qd @ np.swapaxes(kd, -1, -2)
+    eq, ek = np.abs(qd - qt), np.abs(kd - kt)
+    # per-element rounding bound, then the product bound |dq||k| + |q||dk| + |dq||dk|
+    sub_q = np.repeat(sq.astype(np.float64), 32, axis=-1)[..., None] * 2.0 ** -10
+    sub_k = np.repeat(sk.astype(np.float64), 32, axis=-1)[..., None] * 2.0 ** -10
+    assert np.all(eq <= 2.0 ** -4 * np.abs(qt) + sub_q * (1 + 1e-9))
+    assert np.all(ek <= 2.0 ** -4 * np.abs(kt) + sub_k * (1 + 1e-9))
+    bound = eq @ np.swapaxes(np.abs(kt), -1, -2) + np.abs(qt) @ np.swapaxes(ek, -1, -2) + eq @ np.swapaxes(ek, -1, -2)
+    assert np.all(np.abs(s_deq - s_true) <= bound * (1 + 1e-9) + 1e-12)
+    assert np.max(np.abs(s_deq - s_true)) < 0.1 * np.max(np.abs(s_true))
+
+
 ALL_PINS = [pin_rows_sum_to_one, pin_single_key, pin_equal_scores, pin_causal_first_row,
             pin_fully_masked_rows, pin_large_scores, pin_torch_sdpa, pin_brute_force_decimal, pin_linearity_and_permutation,
             pin_gqa, pin_row_selection, pin_exercise1, pin_online_equals_full, pin_merge_orders,
             pin_split_combine, pin_lse_matches_state, pin_bwd_finite_differences, pin_bwd_d_identity,
-            pin_bwd_single_key]
+            pin_bwd_single_key, pin_e4m3_codec, pin_fwht_exact, pin_fp8_quantize_composition,
+            pin_fp8_block_edges, pin_fp8_scores_preserved]

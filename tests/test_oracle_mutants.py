@@ -45,6 +45,17 @@ MUTANTS = [
      "acc += widen(a->dO, a->dtype, q_off + k) * widen(a->K, a->dtype, (kv_head + j) * d + k);"),
     ("bwd_causal_ignored", "        if (a->causal) {\n                int64_t last = i + N_k - N_q;", "        if (0) {\n                int64_t last = i + N_k - N_q;"),
     ("bwd_no_max_shift_unnormalised", "for (int64_t j = 0; j < j_end; ++j) p[j] /= l;", ""),
+    ("e4m3_ties_away", "double m8 = nearbyint(ldexp(a, 3 - e)) - 8.0;", "double m8 = round(ldexp(a, 3 - e)) - 8.0;"),
+    ("e4m3_subnormal_step", "double q = nearbyint(ldexp(a, 9));", "double q = nearbyint(ldexp(a, 10));"),
+    ("e4m3_saturates", "if (isnan(x) || a > 464.0) return (uint8_t)(sign | 0x7F);",
+     "if (isnan(x) || a > 464.0) return (uint8_t)(sign | 0x7E);"),
+    ("fwht_sign_swapped", "x[i + len] = a - b;", "x[i + len] = b - a;"),
+    ("fwht_stage_skipped", "for (int64_t len = 1; len < d; len <<= 1)", "for (int64_t len = 2; len < d; len <<= 1)"),
+    ("fp8_sign_hi_ignored", "(int)((sign_hi >> (j - 64)) & 1u)", "(int)((sign_lo >> (j - 64)) & 1u)"),
+    ("fp8_no_post_scale", "(amax / 448.0f) * post_scale", "(amax / 448.0f)"),
+    ("fp8_fnuz_max", "448.0f / amax", "240.0f / amax"),
+    ("fp8_amax_first_row", "for (int64_t j = 0; j < d; ++j)\n                    if (fabsf(x[j]) > amax) amax = fabsf(x[j]);",
+     "for (int64_t j = 0; j < d; ++j)\n                    if (r == r0 && fabsf(x[j]) > amax) amax = fabsf(x[j]);"),
 ]
 
 
