@@ -8,6 +8,8 @@ memory and to name the stream.
 
     fwd(q, k, v, causal=False, scale=None)   -> (o, lse)          fa_fwd
     bwd(q, k, v, o, lse, do, causal, scale)  -> (dq, dk, dv)      fa_bwd
+    fp8_quantize(q, k, v, signs, incoherent) -> (q8, k8, vt8, qs, ks, vs)  fa_fp8_quantize
+    fwd_fp8(q8, k8, vt8, qs, ks, vs, causal, scale) -> (o, lse)  fa_fwd_fp8
     decode_split(q, k, v, num_splits, scale) -> (o_part, lse_part) fa_decode_split
     combine(o_part, lse_part)                -> (o, lse)          fa_combine
     decode(q, k, v, num_splits=None, scale)  -> (o, lse)          both, on one stream
@@ -18,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "decode_split", "decode_split_paged", "combine", "decode", "decode_num_splits",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "fp8_quantize", "fwd_fp8", "fp8_block_rows", "decode_split", "decode_split_paged", "combine", "decode", "decode_num_splits",
            "decode_workspace_bytes",
            "fwd_tile_shape", "fwd_tile_count", "strerror", "library", "library_path", "FAError"]
 
@@ -52,6 +54,11 @@ def library():
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
         lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        u64 = ctypes.c_uint64
+        lib.fa_fp8_quantize.argtypes = [vp, vp, vp, i32, u64, u64, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                        i32, vp]
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_fp8_block_rows.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
         lib.fa_decode_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
         lib.fa_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                               f32, vp]
@@ -64,7 +71,7 @@ def library():
         lib.fa_fwd_tile_count.restype = ctypes.c_longlong
         lib.fa_strerror.argtypes = [i32]
         lib.fa_strerror.restype = ctypes.c_char_p
-        for fn in (lib.fa_fwd, lib.fa_bwd, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits,
+        for fn in (lib.fa_fwd, lib.fa_bwd, lib.fa_fp8_quantize, lib.fa_fwd_fp8, lib.fa_fp8_block_rows, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits,
                    lib.fa_fwd_tile_shape):
             fn.restype = i32
         _lib = lib
@@ -176,6 +183,70 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, d
 
 def bwd_workspace_bytes(B: int, H: int, N_q: int) -> int:
     return int(library().fa_bwd_workspace_bytes(B, H, N_q))
+
+
+def fp8_block_rows():
+    """(query rows, keys) per FP8 quantisation block."""
+    a, b = ctypes.c_int(), ctypes.c_int()
+    _check("fa_fp8_block_rows", library().fa_fp8_block_rows(ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def fp8_quantize(q, k, v, sign_lo: int = 0, sign_hi: int = 0, incoherent: bool = True):
+    """fa_fp8_quantize.  q [B,H,N_q,d], k/v [B,H_kv,N_k,d] bf16 -> (q8, k8, vt8, q_scale, k_scale,
+    v_scale): e4m3 codes as uint8 (q8 like q, k8 like k, vt8 [B,H_kv,T_c,d,64]) and fp32 block
+    scales.  sign_lo / sign_hi: the 128-bit random sign mask of the transform."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, H, N_q, d = q.shape
+    Bk, H_kv, N_k, dk_ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk_ != d:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    qr, kr = fp8_block_rows()
+    TQ, TC = -(-N_q // qr), -(-N_k // kr)
+    dev = q.device
+    q8 = torch.empty((B, H, N_q, d), dtype=torch.uint8, device=dev)
+    k8 = torch.empty((B, H_kv, N_k, d), dtype=torch.uint8, device=dev)
+    vt8 = torch.empty((B, H_kv, TC, d, kr), dtype=torch.uint8, device=dev)
+    qs = torch.empty((B, H, TQ), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, H_kv, TC), dtype=torch.float32, device=dev)
+    vs = torch.empty((B, H_kv, TC), dtype=torch.float32, device=dev)
+    _check("fa_fp8_quantize", library().fa_fp8_quantize(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), int(bool(incoherent)), int(sign_lo) & (2**64 - 1),
+        int(sign_hi) & (2**64 - 1), q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs.data_ptr(), ks.data_ptr(),
+        vs.data_ptr(), B, H, H_kv, N_q, N_k, d, _stream_ptr(q)))
+    return q8, k8, vt8, qs, ks, vs
+
+
+def fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None, out=None,
+            lse=None):
+    """fa_fwd_fp8 on fp8_quantize's outputs -> o [B,H,N_q,d] bf16, lse [B,H,N_q] fp32."""
+    torch = _torch()
+    _need(q8, "q8", torch.uint8, 4)
+    _need(k8, "k8", torch.uint8, 4)
+    _need(vt8, "vt8", torch.uint8, 5)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, n, torch.float32, 3)
+    B, H, N_q, d = q8.shape
+    Bk, H_kv, N_k, dk_ = k8.shape
+    qr, kr = fp8_block_rows()
+    TQ, TC = -(-N_q // qr), -(-N_k // kr)
+    if (Bk != B or dk_ != d or tuple(vt8.shape) != (B, H_kv, TC, d, kr) or tuple(q_scale.shape) != (B, H, TQ)
+            or tuple(k_scale.shape) != (B, H_kv, TC) or tuple(v_scale.shape) != (B, H_kv, TC)):
+        raise ValueError("fp8 operand shapes do not match fp8_quantize's layout")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N_q, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q8.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _check("fa_fwd_fp8", library().fa_fwd_fp8(
+        q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+        out.data_ptr(), lse.data_ptr(), B, H, H_kv, N_q, N_k, d, int(bool(causal)), float(scale), _stream_ptr(q8)))
+    return out, lse
 
 
 def decode_split(q, k, v, num_splits: int, scale: float | None = None, o_part=None, lse_part=None):

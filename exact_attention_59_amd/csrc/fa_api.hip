@@ -59,7 +59,7 @@ FA_EXPORT const char* fa_strerror(int status) {
         case FA_ERR_SHAPE: return "invalid shape (a size <= 0, H not a multiple of H_kv, or num_splits outside [1, N_k])";
         case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dimension must be 64 or 128, or a size exceeds the limits)";
         case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-        case FA_ERR_ARG: return "invalid argument (scale not finite, or causal not 0/1)";
+        case FA_ERR_ARG: return "invalid argument (scale not finite and positive, or a flag not 0/1)";
         case FA_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
         default: return "unknown status";
     }
@@ -99,7 +99,7 @@ FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float
     const long long blocks = (long long)((N_q + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * H;
     if (blocks > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(LSE)) return FA_ERR_ALIGN;
-    if (!isfinite(scale)) return FA_ERR_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
     if (debug_enabled())
         fprintf(stderr, "[fa] fwd B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d causal=%d blocks=%lld\n", B, H, H_kv, N_q,
@@ -125,7 +125,7 @@ FA_EXPORT int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
     if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(dO) || misaligned(LSE) ||
         misaligned(dQ) || misaligned(dK) || misaligned(dV) || misaligned(workspace))
         return FA_ERR_ALIGN;
-    if (!isfinite(scale)) return FA_ERR_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
     if (debug_enabled())
         fprintf(stderr, "[fa] bwd B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d causal=%d\n", B, H, H_kv, N_q, N_k, d, causal);
@@ -137,6 +137,60 @@ FA_EXPORT int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
 FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int H, int N_q) {
     if (B <= 0 || H <= 0 || N_q <= 0) return 0;
     return (size_t)B * H * N_q * sizeof(float);
+}
+
+FA_EXPORT int fa_fp8_block_rows(int* q_rows, int* kv_rows) {
+    if (q_rows) *q_rows = fa::kFp8QRows;
+    if (kv_rows) *kv_rows = fa::kFp8KRows;
+    return FA_OK;
+}
+
+FA_EXPORT int fa_fp8_quantize(const void* Q, const void* K, const void* V, int incoherent, uint64_t sign_lo,
+                              uint64_t sign_hi, void* Q8, void* K8, void* Vt8, float* q_scale, float* k_scale,
+                              float* v_scale, int B, int H, int H_kv, int N_q, int N_k, int d, void* stream) {
+    if (!Q || !K || !V || !Q8 || !K8 || !Vt8 || !q_scale || !k_scale || !v_scale) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_q <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
+    if (H % H_kv) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * N_q * d >= kMaxElems || (long long)B * H_kv * (N_k + fa::kFp8KRows) * d >= kMaxElems)
+        return FA_ERR_UNSUPPORTED;
+    const long long tq = (N_q + fa::kFp8QRows - 1) / fa::kFp8QRows, tk = (N_k + fa::kFp8KRows - 1) / fa::kFp8KRows;
+    if ((long long)B * H * tq + 2LL * B * H_kv * tk > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(Q8) || misaligned(K8) || misaligned(Vt8) ||
+        (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+        return FA_ERR_ALIGN;
+    if (incoherent != 0 && incoherent != 1) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] fp8_quantize B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d incoherent=%d\n", B, H, H_kv, N_q, N_k,
+                d, incoherent);
+    return finish(fa::launch_fp8_quantize(Q, K, V, incoherent, sign_lo, sign_hi, Q8, K8, Vt8, q_scale, k_scale,
+                                          v_scale, B, H, H_kv, N_q, N_k, d, static_cast<hipStream_t>(stream)),
+                  "fa_fp8_quantize");
+}
+
+FA_EXPORT int fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
+                         const float* v_scale, void* O, float* LSE, int B, int H, int H_kv, int N_q, int N_k, int d,
+                         int causal, float scale, void* stream) {
+    if (!Q8 || !K8 || !Vt8 || !q_scale || !k_scale || !v_scale || !O || !LSE) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_q <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
+    if (H % H_kv) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * N_q * d >= kMaxElems || (long long)B * H_kv * (N_k + fa::kFp8KRows) * d >= kMaxElems)
+        return FA_ERR_UNSUPPORTED;
+    const long long blocks = (long long)((N_q + fa::kFp8QRows - 1) / fa::kFp8QRows) * B * H;
+    if (blocks > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (misaligned(Q8) || misaligned(K8) || misaligned(Vt8) || misaligned(O) || misaligned(LSE) ||
+        (reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+        return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] fwd_fp8 B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d causal=%d\n", B, H, H_kv, N_q, N_k, d, causal);
+    return finish(fa::launch_fwd_fp8(Q8, K8, Vt8, q_scale, k_scale, v_scale, O, LSE, B, H, H_kv, N_q, N_k, d,
+                                     causal == 1, scale, static_cast<hipStream_t>(stream)),
+                  "fa_fwd_fp8");
 }
 
 FA_EXPORT int fa_decode_split(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
@@ -154,7 +208,7 @@ FA_EXPORT int fa_decode_split(const void* Q, const void* K, const void* V, float
     if ((long long)num_splits * n_qc * B * H_kv > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O_part) || misaligned(LSE_part))
         return FA_ERR_ALIGN;
-    if (!isfinite(scale)) return FA_ERR_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
     if (debug_enabled())
         fprintf(stderr, "[fa] decode_split B=%d H=%d H_kv=%d N_k=%d d=%d S=%d\n", B, H, H_kv, N_k, d, num_splits);
     return finish(fa::launch_decode_split(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, d, num_splits, scale,
@@ -185,7 +239,7 @@ FA_EXPORT int fa_decode_split_paged(const void* Q, const void* K_pages, const vo
     if (misaligned(Q) || misaligned(K_pages) || misaligned(V_pages) || misaligned(O_part) || misaligned(LSE_part) ||
         (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
         return FA_ERR_ALIGN;
-    if (!isfinite(scale)) return FA_ERR_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
     if (debug_enabled())
         fprintf(stderr, "[fa] decode_split_paged B=%d H=%d H_kv=%d P=%d max_pages=%d num_pages=%d d=%d S=%d\n", B, H,
                 H_kv, page_size, max_pages, num_pages, d, num_splits);

@@ -57,20 +57,6 @@ __device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ src, int
     }
 }
 
-// Workgroup id -> (head index, rank): the workgroups of one head on one XCD when the head
-// count is a multiple of 8 (their shared operand tiles then meet in that XCD's L2).
-__device__ __forceinline__ void map_block_bwd(int bid, int n_ranks, int n_heads, int& head, int& rank) {
-    if ((n_heads & 7) == 0) {
-        const int xcd = bid & 7, li = bid >> 3;
-        const int hl = li / n_ranks;
-        rank = li - hl * n_ranks;
-        head = xcd + 8 * hl;
-    } else {
-        rank = bid / n_heads;
-        head = bid - rank * n_heads;
-    }
-}
-
 // Per-lane read offsets shared by both main kernels (elements within one LDS tile):
 //   row_off[ks]: an operand along d -- row l32, logical chunk 2*ks + hh;
 //   tr_lo[db], tr_hi[db]: the two transposing reads of a 32-d x 16-row slice (see the
@@ -169,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
     int bh, rank;
-    map_block_bwd(blockIdx.x, T_r, BH, bh, rank);
+    map_block_xcd(blockIdx.x, T_r, BH, bh, rank);
     const int q_tile = CAUSAL ? T_r - 1 - rank : rank;  // causal: long tiles dispatch first
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / H_kv);
@@ -307,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
     int bg, kt;
-    map_block_bwd(blockIdx.x, T_k, BG, bg, kt);
+    map_block_xcd(blockIdx.x, T_k, BG, bg, kt);
     const int b = bg / H_kv, g = bg - b * H_kv;
     const int group = H / H_kv;
     const int64_t kv_base = (int64_t)bg * N_k * D;
@@ -462,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const bool ds_wave = w >= 4;
     const int l32 = lane & 31, hh = lane >> 5;
     int bg, kt;
-    map_block_bwd(blockIdx.x, T_k, BG, bg, kt);
+    map_block_xcd(blockIdx.x, T_k, BG, bg, kt);
     const int b = bg / H_kv, g = bg - b * H_kv;
     const int group = H / H_kv;
     const int64_t kv_base = (int64_t)bg * N_k * D;

@@ -28,6 +28,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr float kLn2 = 0.693147180559945309417f;
@@ -38,6 +39,39 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands OCP e4m3 and unit block scales
+// (E8M0 exponent 127 = 2^0): D[32x32] += A[32x64] * B[64x32] in fp32.  Each lane holds 32
+// e4m3 bytes of A (row l % 32) and of B (column l % 32); byte e of lane l's A pairs with
+// byte e of lane l' = (n + 32 * (l / 32))'s B -- the 64-deep contraction runs over the
+// slots (l / 32, e), numbered alike in both operands (established by an on-GPU probe).
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Round two floats to OCP e4m3 (nearest-even; NaN beyond 464) into bytes 0-1 (HI = false)
+// or 2-3 (HI = true) of `old`, keeping its other half (v_cvt_pk_fp8_f32).
+template <bool HI>
+__device__ __forceinline__ int pack_fp8x2(float a, float b, int old) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+// Workgroup id -> (head index, rank within the head).  Consecutive ids are dispatched
+// round-robin over the 8 XCDs, each with its own L2.  When the head count is a multiple of
+// 8, every workgroup of a head goes to the same XCD (id % 8 == head % 8) and, within an
+// XCD, ids walk head by head, so the workgroups of a head are resident together and share
+// the head's tiles in that L2.  Otherwise ids go rank-major over all heads.
+__device__ __forceinline__ void map_block_xcd(int bid, int n_ranks, int n_heads, int& head, int& rank) {
+    if ((n_heads & 7) == 0) {
+        const int xcd = bid & 7, li = bid >> 3;
+        const int hl = li / n_ranks;
+        rank = li - hl * n_ranks;
+        head = xcd + 8 * hl;
+    } else {
+        rank = bid / n_heads;
+        head = bid - rank * n_heads;
+    }
 }
 
 // 2^x on the transcendental unit (v_exp_f32); exact at x = 0, 0 at -inf.

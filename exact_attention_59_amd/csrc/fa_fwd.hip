@@ -70,23 +70,6 @@ __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 
 // whatever m is used, it cancels between the numerator acc and the denominator l.
 constexpr float kRescaleSlack = 8.0f;
 
-// Workgroup id -> (b*H + h, rank).  Consecutive ids are dispatched round-robin over the 8
-// XCDs, each with its own L2.  When B*H is a multiple of 8, every workgroup of a head goes
-// to the same XCD (id % 8 == head % 8) and, within an XCD, ids walk head by head, so the
-// workgroups of a head are resident together and each K/V tile is fetched into L2 once
-// and shared.  Otherwise ids go rank-major over all heads.
-__device__ __forceinline__ void map_block(int bid, int n_ranks, int BH, int& bh, int& rank) {
-    if ((BH & 7) == 0) {
-        const int xcd = bid & 7, li = bid >> 3;
-        const int hl = li / n_ranks;
-        rank = li - hl * n_ranks;
-        bh = xcd + 8 * hl;
-    } else {
-        rank = bid / BH;
-        bh = bid - rank * BH;
-    }
-}
-
 // Two workgroups (8 waves) per CU.  (Three fit at d = 64 but measured no faster: the
 // loop is bound by LDS read throughput, not by latency.)
 template <int D>
@@ -121,7 +104,7 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     // query tiles (T_r-1-rank, rank): every workgroup then carries the same work.
     const int n_ranks = CAUSAL ? (T_r + 1) / 2 : T_r;
     int bh, rank;
-    map_block(blockIdx.x, n_ranks, BH, bh, rank);
+    map_block_xcd(blockIdx.x, n_ranks, BH, bh, rank);
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / H_kv);
     const int64_t q_base = (int64_t)bh * N_q * D;

@@ -19,6 +19,11 @@ constexpr int bwd_dq_block_cols(int d) { return d == 128 ? 32 : 64; }
 constexpr int kBwdBlockKeys = 128;
 constexpr int kBwdBlockQueries = 32;
 
+// FP8 path: rows per quantisation block of Q (= the forward's query tile) and of K / V
+// (= the forward's key tile).
+constexpr int kFp8QRows = 128;
+constexpr int kFp8KRows = 64;
+
 // Decode: keys per wave iteration and query heads per workgroup.
 constexpr int kDecKeysPerWave = 32;
 constexpr int kDecHeadsPerBlock = 16;
@@ -30,6 +35,14 @@ hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, floa
 hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                       void* dQ, void* dK, void* dV, float* workspace, int B, int H, int H_kv, int N_q, int N_k, int d,
                       bool causal, float scale, hipStream_t stream);
+
+hipError_t launch_fp8_quantize(const void* Q, const void* K, const void* V, int transform, uint64_t sign_lo,
+                               uint64_t sign_hi, void* Q8, void* K8, void* Vt8, float* q_scale, float* k_scale,
+                               float* v_scale, int B, int H, int H_kv, int N_q, int N_k, int d, hipStream_t stream);
+
+hipError_t launch_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
+                          const float* v_scale, void* O, float* LSE, int B, int H, int H_kv, int N_q, int N_k, int d,
+                          bool causal, float scale, hipStream_t stream);
 
 hipError_t launch_decode_split(const void* Q, const void* K, const void* V, float* O_part,
                                float* LSE_part, int B, int H, int H_kv, int N_k, int d, int num_splits,

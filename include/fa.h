@@ -14,6 +14,9 @@
  *                    (block table, per-sequence lengths).
  *   fa_combine       flash-decoding, step 3: exact merge of the segments by
  *                    log-sum-exp.
+ *   fa_fp8_quantize  FP8 path, step 1: random-sign Hadamard transform of Q and K
+ *                    and e4m3 block quantisation of Q, K, V.
+ *   fa_fwd_fp8       FP8 path, step 2: the forward on fp8 matrix cores.
  * Sources: Lecture 11, "Kernel Optimization Techniques: FlashAttention,
  * flash-decoding and megakernel", sections 2-6; the FlashAttention v1 and v2
  * cards of the "CUDA Kernel interview course" page.
@@ -43,6 +46,7 @@
 #define FA_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -54,7 +58,7 @@ typedef enum {
     FA_ERR_SHAPE = 2,       /* a size is <= 0, H % H_kv != 0, or num_splits out of range */
     FA_ERR_UNSUPPORTED = 3, /* head dimension d not in {64, 128}, or a size beyond the limits below */
     FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
-    FA_ERR_ARG = 5,         /* scale not finite, or causal not 0/1 */
+    FA_ERR_ARG = 5,         /* scale not finite and positive, or a 0/1 flag out of range */
     FA_ERR_HIP = 6          /* the HIP runtime reported an error when enqueueing */
 } fa_status;
 
@@ -69,7 +73,8 @@ typedef enum {
  *   LSE [B][H][N_q]       fp32, written (natural log)
  *   causal: 0 = no mask; 1 = bottom-right aligned causal mask, query i sees key j
  *           iff j <= i + N_k - N_q (the lower triangle when N_q == N_k).
- *   scale: multiplies q . k (usually 1/sqrt(d)); must be finite.
+ *   scale: multiplies q . k (usually 1/sqrt(d)); must be finite and > 0 (the row max
+ *          is taken on unscaled scores).
  * Limits: d in {64, 128}; B*H*N_q*d and B*H_kv*N_k*d below 2^62.
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
@@ -102,6 +107,50 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
 
 /* Bytes of workspace fa_bwd needs: 4 * B * H * N_q (0 if a size is <= 0). */
 size_t fa_bwd_workspace_bytes(int B, int H, int N_q);
+
+/*
+ * FP8 (OCP e4m3) forward, in two calls.  What the pages fix (the FlashAttention v3 card of
+ * the CUDA Kernel interview course, "FP8 path"; Lecture 11 section 4.4): one scale per
+ * block, and a random orthogonal transform applied first so that outlier channels are
+ * spread over all channels.  Readings taken where they are silent:
+ *   - e4m3 = OCP e4m3fn (bias 7, largest finite 448, subnormals to 2^-9), nearest-even;
+ *   - the transform is x -> (s o x) H with H the unnormalised Sylvester-Hadamard matrix
+ *     (H H^T = d I) and s the signs given by the 128-bit mask (bit j of sign_hi:sign_lo set
+ *     means channel j is negated); it is applied to Q and K (scores are unchanged up to the
+ *     factor d, which the query scales carry), never to V;
+ *   - blocks: 128 query rows, 64 keys (the forward's tiles; fa_fp8_block_rows);
+ *     amax = max |x| over the block, code = e4m3(x * (448 / amax)) computed in fp32,
+ *     scale = amax / 448 (times 1/d for transformed queries); all-zero block: scale 0.
+ * Dequantised values are code * scale; the product of a dequantised query and key is the
+ * original score up to rounding.
+ *
+ * fa_fp8_quantize: Q [B][H][N_q][d], K and V [B][H_kv][N_k][d] bf16, read.  Written:
+ *   Q8      [B][H][N_q][d]       e4m3 bytes
+ *   K8      [B][H_kv][N_k][d]    e4m3 bytes
+ *   Vt8     [B][H_kv][T_c][d][64] e4m3 bytes, T_c = ceil(N_k / 64): tile t of key/value head
+ *           (b, g) holds, in row j and position p = 32 h + e (h < 2, e < 32), the code of
+ *           V[64 t + 32 (e/16) + 8 ((e%16)/4) + 4 h + e%4][j] (zero past N_k): each tile is
+ *           transposed and its keys permuted into the order the forward's operands use
+ *   q_scale [B][H][ceil(N_q / 128)] fp32;  k_scale, v_scale [B][H_kv][T_c] fp32
+ *   incoherent: 1 = apply the transform, 0 = quantise Q and K as they are.
+ * The codes and scales are a deterministic function of the inputs (bit-exact).
+ * Alignment: tensors 16 bytes, scale arrays 4 bytes.
+ *
+ * fa_fwd_fp8: exact attention of the dequantised Q, K, V -- softmax(scale * q . k) v with
+ * q . k = (Q8 q_scale) . (K8 k_scale) -- computed tile by tile as fa_fwd does, with P
+ * rounded to e4m3 for the P V product.  O [B][H][N_q][d] bf16 and LSE [B][H][N_q] fp32 are
+ * written; causal and scale as for fa_fwd.  All other arguments are fa_fp8_quantize's
+ * outputs for the same shapes.
+ */
+int fa_fp8_block_rows(int* q_rows, int* kv_rows);
+
+int fa_fp8_quantize(const void* Q, const void* K, const void* V, int incoherent, uint64_t sign_lo, uint64_t sign_hi,
+                    void* Q8, void* K8, void* Vt8, float* q_scale, float* k_scale, float* v_scale, int B, int H,
+                    int H_kv, int N_q, int N_k, int d, void* stream);
+
+int fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
+               const float* v_scale, void* O, float* LSE, int B, int H, int H_kv, int N_q, int N_k, int d, int causal,
+               float scale, void* stream);
 
 /*
  * Flash-decoding split step (Lecture 11 section 6.2, steps 1-2): one query token

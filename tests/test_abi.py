@@ -37,7 +37,8 @@ def exported_symbols(path):
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_split", "fa_decode_split_paged", "fa_combine", "fa_decode_num_splits",
+    for want in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fp8_quantize", "fa_fwd_fp8", "fa_fp8_block_rows",
+                 "fa_decode_split", "fa_decode_split_paged", "fa_combine", "fa_decode_num_splits",
                  "fa_decode_workspace_bytes", "fa_strerror", "fa_fwd_tile_shape", "fa_fwd_tile_count"):
         assert want in names
 
@@ -75,6 +76,7 @@ def bwd(lib, Q=P, K=P, V=P, O=P, dO=P, L=P, dQ=P, dK=P, dV=P, W=P, B=1, H=2, H_k
     (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(dO=P_MIS), fa.FA_ERR_ALIGN), (dict(dK=P_MIS), fa.FA_ERR_ALIGN), (dict(W=P_MIS), fa.FA_ERR_ALIGN),
     (dict(scale=float("inf")), fa.FA_ERR_ARG), (dict(causal=3), fa.FA_ERR_ARG),
+    (dict(scale=0.0), fa.FA_ERR_ARG), (dict(scale=-0.125), fa.FA_ERR_ARG),
 ])
 def test_bwd_validation(lib, kw, status):
     assert bwd(lib, **kw) == status
@@ -84,6 +86,40 @@ def test_bwd_workspace_bytes(lib):
     assert fa.bwd_workspace_bytes(2, 16, 1000) == 2 * 16 * 1000 * 4
     assert fa.bwd_workspace_bytes(0, 16, 1000) == 0
     assert fa.bwd_workspace_bytes(1, 1, -3) == 0
+
+
+def q8(lib, Q=P, K=P, V=P, inc=1, Q8=P, K8=P, Vt=P, qs=P, ks=P, vs=P, B=1, H=2, H_kv=1, N_q=8, N_k=8, d=64):
+    return lib.fa_fp8_quantize(Q, K, V, inc, 1, 2, Q8, K8, Vt, qs, ks, vs, B, H, H_kv, N_q, N_k, d, None)
+
+
+def f8(lib, Q8=P, K8=P, Vt=P, qs=P, ks=P, vs=P, O=P, L=P, B=1, H=2, H_kv=1, N_q=8, N_k=8, d=64, causal=0, scale=0.125):
+    return lib.fa_fwd_fp8(Q8, K8, Vt, qs, ks, vs, O, L, B, H, H_kv, N_q, N_k, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(Vt=None), fa.FA_ERR_NULL), (dict(vs=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(N_k=-2), fa.FA_ERR_SHAPE), (dict(H=3, H_kv=2), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(Q8=P_MIS), fa.FA_ERR_ALIGN), (dict(Vt=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(qs=ctypes.c_void_p(0x100002)), fa.FA_ERR_ALIGN), (dict(inc=2), fa.FA_ERR_ARG),
+])
+def test_fp8_quantize_validation(lib, kw, status):
+    assert q8(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q8=None), fa.FA_ERR_NULL), (dict(ks=None), fa.FA_ERR_NULL), (dict(L=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=5, H_kv=2), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(O=P_MIS), fa.FA_ERR_ALIGN), (dict(K8=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(scale=0.0), fa.FA_ERR_ARG), (dict(scale=float("nan")), fa.FA_ERR_ARG), (dict(causal=2), fa.FA_ERR_ARG),
+])
+def test_fwd_fp8_validation(lib, kw, status):
+    assert f8(lib, **kw) == status
+
+
+def test_fp8_scale_arrays_need_only_4_bytes(lib):
+    four = ctypes.c_void_p(0x100004)
+    assert q8(lib, qs=four, ks=four, vs=four, inc=2) == fa.FA_ERR_ARG  # alignment passes, the flag fails
+    assert fa.fp8_block_rows() == (128, 64)
 
 
 def dec(lib, Q=P, K=P, V=P, Op=P, Lp=P, B=1, H=4, H_kv=1, N_k=64, d=128, S=4, scale=0.1):
@@ -104,6 +140,7 @@ def comb(lib, Op=P, Lp=P, O=P, L=P, B=1, H=4, d=128, S=4):
     (dict(Q=P_MIS), fa.FA_ERR_ALIGN), (dict(O=P_MIS), fa.FA_ERR_ALIGN), (dict(L=P_MIS), fa.FA_ERR_ALIGN),
     (dict(scale=float("inf")), fa.FA_ERR_ARG), (dict(scale=float("nan")), fa.FA_ERR_ARG),
     (dict(causal=2), fa.FA_ERR_ARG), (dict(causal=-1), fa.FA_ERR_ARG),
+    (dict(scale=0.0), fa.FA_ERR_ARG), (dict(scale=-0.125), fa.FA_ERR_ARG), (dict(scale=-0.0), fa.FA_ERR_ARG),
 ])
 def test_fwd_validation(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -115,7 +152,7 @@ def test_fwd_validation(lib, kw, status):
     (dict(S=0), fa.FA_ERR_SHAPE), (dict(S=65), fa.FA_ERR_SHAPE),
     (dict(d=80), fa.FA_ERR_UNSUPPORTED), (dict(H=65, H_kv=1), fa.FA_ERR_UNSUPPORTED),
     (dict(K=P_MIS), fa.FA_ERR_ALIGN), (dict(Lp=P_MIS), fa.FA_ERR_ALIGN),
-    (dict(scale=float("-inf")), fa.FA_ERR_ARG),
+    (dict(scale=float("-inf")), fa.FA_ERR_ARG), (dict(scale=0.0), fa.FA_ERR_ARG), (dict(scale=-1.0), fa.FA_ERR_ARG),
 ])
 def test_decode_validation(lib, kw, status):
     assert dec(lib, **kw) == status
@@ -141,7 +178,7 @@ P_ODD = ctypes.c_void_p(0x100002)   # 2-byte aligned
     (dict(page=8192), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(H=65, H_kv=1), fa.FA_ERR_UNSUPPORTED),
     (dict(K=P_MIS), fa.FA_ERR_ALIGN), (dict(T=P_ODD), fa.FA_ERR_ALIGN), (dict(Ls=P_ODD), fa.FA_ERR_ALIGN),
-    (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG), (dict(scale=-0.5), fa.FA_ERR_ARG),
 ])
 def test_decode_paged_validation(lib, kw, status):
     assert paged(lib, **kw) == status
