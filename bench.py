@@ -11,7 +11,8 @@ then combine kernel) runs in the same invocation and is reported under "decode" 
 GB/s of K+V read once, against the 8 TB/s HBM peak; a 640 MB read sweep before every
 timed decode repetition evicts K/V from the 256 MB last-level cache.  The backward leg
 (fa_bwd on the same prefill shape) is reported under "backward", in TFLOP/s of its five
-N_q x N_k x d products.
+N_q x N_k x d products.  The FP8 leg (quantiser + e4m3 forward) is reported under "fp8",
+against the 5.03 PFLOP/s dense fp8 peak.
 
 Inputs are synthetic and seeded (counter-based SplitMix64 + Box-Muller, see gen/),
 already resident in device memory when timing starts.  GPU times come from HIP
@@ -36,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 (e4m3) MFMA, twice the bf16 rate
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attn fwd TFLOPS & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
@@ -203,6 +205,54 @@ def leg_backward(fa, torch, reps, B=16, H=16, H_kv=16, N=1024, seed=2):
             "5 * 2*B*H*N_q*N_k*d, halved under the causal mask (the backward's five products)", "runs": res}
 
 
+def leg_fp8(fa, torch, reps):
+    """FP8 path: fa_fp8_quantize (HBM-bound: bf16 Q, K, V read, e4m3 codes written) and
+    fa_fwd_fp8 (fp8 matrix cores) on the batched-prefill shape (both masks) and the
+    long-sequence causal shape; the same nominal flops as the bf16 forward."""
+    import gen
+
+    runs = {}
+    for name, seed, B, H, N, d, causal in (("batched prefill d=64 non-causal", 2, 16, 16, 1024, 64, False),
+                                           ("batched prefill d=64 causal", 2, 16, 16, 1024, 64, True),
+                                           ("long causal B=2 H=16 N=8192 d=128", 3, 2, 16, 8192, 128, True)):
+        Q, K, V = fwd_inputs(seed, B, H, H, N, d)
+        q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
+        lo, hi = (int(w) for w in gen.words(seed, 4, 0, 2))
+        g = fa.fp8_quantize(q, k, v, lo, hi, True)
+        o, lse = fa.fwd_fp8(*g, causal=causal)
+        stream = torch.cuda.current_stream()
+
+        def timed(fn):
+            w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            w0.record(stream)
+            while True:  # >= 30 ms first
+                for _ in range(10):
+                    fn()
+                w1.record(stream)
+                w1.synchronize()
+                if w0.elapsed_time(w1) >= 30.0:
+                    break
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(stream)
+            for i in range(reps):
+                fn()
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps
+
+        t_q = timed(lambda: fa.fp8_quantize(q, k, v, lo, hi, True))
+        t_f = timed(lambda: fa.fwd_fp8(*g, causal=causal, out=o, lse=lse))
+        fl = fwd_flops(B, H, N, N, d, causal)
+        qbytes = 3.0 * B * H * N * d * 2 + 3.0 * B * H * N * d + 4.0 * (B * H * (-(-N // 128)) + 2 * B * H * (-(-N // 64)))
+        runs[name] = {"fwd_us": round(t_f * 1e3, 2), "fwd_tflops": round(fl / (t_f * 1e-3) / 1e12, 1),
+                      "pct_fp8_peak": round(100.0 * fl / (t_f * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+                      "quantize_us": round(t_q * 1e3, 2), "quantize_GBs": round(qbytes / (t_q * 1e-3) / 1e9, 1),
+                      "quantize_pct_hbm_peak": round(100.0 * qbytes / (t_q * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        del q, k, v, g, o, lse
+    return {"workload": "e4m3 forward with random-sign Hadamard transform, per-block scales (128 query rows, "
+                        "64 keys)", "peak_fp8_tflops": PEAK_FP8_TFLOPS, "runs": runs}
+
+
 def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=None):
     import gen
 
@@ -338,7 +388,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
-    ap.add_argument("--legs", default="fwd,decode,bwd,cpu", help="comma list of fwd, decode, bwd, cpu, copy")
+    ap.add_argument("--legs", default="fwd,decode,bwd,fp8,cpu", help="comma list of fwd, decode, bwd, fp8, cpu, copy")
     ap.add_argument("--all", action="store_true", help="also time the long-sequence and GQA forward workloads")
     ap.add_argument("--decode-reps", type=int, default=30)
     ap.add_argument("--decode-nk", default="4096,65536", help="comma list of decode cache lengths")
@@ -409,6 +459,12 @@ def main():
         log("backward leg")
         out["backward"] = leg_backward(fa, torch, 30)
         log("backward", out["backward"])
+        torch.cuda.empty_cache()
+
+    if "fp8" in legs:
+        log("fp8 leg")
+        out["fp8"] = leg_fp8(fa, torch, 30)
+        log("fp8", out["fp8"])
         torch.cuda.empty_cache()
 
     if args.all:
