@@ -10,6 +10,15 @@
     # or, with several runs (decode kernels of different cache lengths share one grid):
     python3 <repo>/bench_counters.py N_k=4096=OUT/f4096,OUT/w4096 N_k=65536=OUT/f65536,OUT/w65536
 
+    # shader counters (MFMA and VALU activity, LDS bank conflicts) of one run:
+    rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA SQ_INSTS_VALU \
+        SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d OUT/sq -o run -- \
+        python3 <repo>/bench.py --legs fwd,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3
+    python3 <repo>/bench_counters.py sq OUT/sq        # -> profiles/sq_counters.md
+    # kernel durations of a plain bench run:
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- python3 <repo>/bench.py
+    python3 <repo>/bench_counters.py trace OUT/trace  # -> profiles/kernel_trace.md
+
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the L2 channels) are scaled by
 what the same counters read for the bench's plain 1 GiB device copy (`--legs copy`):
 factor = known bytes / counted bytes, separately for reads and writes.  The result goes
@@ -66,8 +75,96 @@ def averages(per) -> dict:
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
+SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8         # GRBM_GUI_ACTIVE is summed over the 8 XCDs (each has its own graphics block)
+SQ_KERNELS = r"(fwd_kernel<\d+, (?:true|false)>|fwd_fp8_kernel<\d+, (?:true|false)>|fp8_quant_kernel<\d+>|" \
+             r"bwd_\w+<\d+(?:, (?:true|false))?>|decode_split_kernel<\d+(?:, (?:true|false))?>|combine_kernel<\d+>)"
+
+
+def sq_summary(run_dir: str, cmd: str) -> str:
+    """Average per dispatch of every SQ counter of a run, per kernel and grid, plus ratios:
+    MFMA busy / busy cycles, VALU-active / wave cycles, LDS bank conflicts per LDS instruction."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            m = re.search(SQ_KERNELS, row["Kernel_Name"])
+            if m:
+                key = "%s grid=%s" % (m.group(1), row["Grid_Size"])
+                per[key][row["Counter_Name"]][(f, row["Dispatch_Id"])] += float(row["Counter_Value"])
+    names = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_MFMA",
+             "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
+    lines = ["# Shader counters per kernel launch (rocprofv3 SQ counters, averages per dispatch)", "",
+             "Command (from /tmp, TMPDIR=/tmp):", "", "    " + cmd, "    python3 <repo>/bench_counters.py sq OUT/sq", "",
+             "GPU cycles = GRBM_GUI_ACTIVE / %d XCDs (the launch's duration in cycles); MFMA busy %% = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles x %d SIMDs); VALU active %% = "
+             "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES (the waves' share of cycles issuing VALU); conflicts / LDS instr = "
+             "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS." % (XCDS, SIMDS), "",
+             "| kernel | GPU cycles | MFMA busy % | VALU active % | MFMA instr | VALU instr | LDS instr | LDS bank conflicts | conflicts / LDS instr |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(per):
+        avg = {n: (sum(per[key][n].values()) / len(per[key][n])) if per[key][n] else float("nan") for n in names}
+        gpu = avg["GRBM_GUI_ACTIVE"] / XCDS
+        lines.append("| %s | %.0f | %.1f | %.1f | %.0f | %.0f | %.0f | %.0f | %.4f |" % (
+            key, gpu, 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS) if gpu else float("nan"),
+            100.0 * avg["SQ_ACTIVE_INST_VALU"] / avg["SQ_WAVE_CYCLES"] if avg["SQ_WAVE_CYCLES"] else float("nan"),
+            avg["SQ_INSTS_MFMA"], avg["SQ_INSTS_VALU"], avg["SQ_INSTS_LDS"], avg["SQ_LDS_BANK_CONFLICT"],
+            avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_INSTS_LDS"] if avg["SQ_INSTS_LDS"] else float("nan")))
+    return "\n".join(lines) + "\n"
+
+
+def trace_summary(run_dir: str, cmd: str, tail: int = 200) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run (csv): per-kernel statistics
+    and per-launch-shape averages (the last `tail` calls of a shape are the bench's
+    back-to-back loop, after its warm-up)."""
+    stats = list(csv.DictReader(open(os.path.join(run_dir, "run_kernel_stats.csv"))))
+    trace = sorted(csv.DictReader(open(os.path.join(run_dir, "run_kernel_trace.csv"))),
+                   key=lambda r: int(r["Start_Timestamp"]))
+
+    def short(n):
+        m = re.search(SQ_KERNELS, n)
+        return m.group(1) if m else n.split("(")[0][:60]
+
+    out = ["# Kernel trace of a bench.py run (all legs but the CPU baseline)", "",
+           "Command (from /tmp, TMPDIR=/tmp):", "", "    " + cmd, "    python3 <repo>/bench_counters.py trace OUT/trace", "",
+           "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        out.append("| %s | %s | %.2f | %.2f | %.2f | %.1f |" % (short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                                                             float(r["Percentage"])))
+    g = defaultdict(list)
+    for r in trace:
+        key = "%s grid=%s" % (short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        g[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out += ["", "Per launch shape (grid = work-items); the last column averages the last %d calls of the shape." % tail,
+            "", "| kernel, grid | calls | average us | min us | last %d average us |" % tail, "|---|---|---|---|---|"]
+    for k, v in sorted(g.items()):
+        if not re.search(SQ_KERNELS, k):
+            continue
+        out.append("| %s | %d | %.2f | %.2f | %.2f |" % (k, len(v), sum(v) / len(v), min(v), sum(v[-tail:]) / len(v[-tail:])))
+    return "\n".join(out) + "\n"
+
+
 def main():
     args = sys.argv[1:]
+    if len(args) == 2 and args[0] == "trace":
+        cmd = "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- python3 <repo>/bench.py"
+        text = trace_summary(args[1], cmd)
+        with open(os.path.join(ROOT, "profiles", "kernel_trace.md"), "w") as f:
+            f.write(text)
+        print(text)
+        return
+    if len(args) == 2 and args[0] == "sq":
+        cmd = ("rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA SQ_INSTS_VALU "
+               "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d OUT/sq -o run -- "
+               "python3 <repo>/bench.py --legs fwd,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3")
+        text = sq_summary(args[1], cmd)
+        with open(os.path.join(ROOT, "profiles", "sq_counters.md"), "w") as f:
+            f.write(text)
+        print(text)
+        return
     if len(args) == 2 and "=" not in args[0]:
         runs = [("", args[0], args[1])]
     elif args and all("=" in a and "," in a for a in args):
