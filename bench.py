@@ -41,6 +41,7 @@ PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 (e4m3) MFMA, twice the bf16 rate
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attn fwd TFLOPS & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+SQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
 KERNEL_SOURCES = ["fa_common.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_decode.hip"]
 
 
@@ -382,6 +383,22 @@ def traffic_from_counters(dominant_kernel_substr):
     return None, "dominant kernel not in the counter summary"
 
 
+def shader_counters(dominant_kernel_substr):
+    """MFMA busy and LDS bank conflicts per launch from the committed shader-counter summary,
+    if the kernel is unchanged (None otherwise)."""
+    try:
+        with open(SQ_COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    for name, k in c.get("kernels", {}).items():
+        if dominant_kernel_substr in name:
+            return dict(k, source="profiles/sq_counters.json (%s)" % name)
+    return None
+
+
 # ---------------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -440,7 +457,8 @@ def main():
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                            "traffic_source": src, "avg_launch_us": round(r["noncausal"]["ms"] * 1e3, 2),
                            "algorithmic_flops_per_launch": r["flops_noncausal"],
-                           "algorithmic_bytes_per_launch": r["bytes_noncausal"]}
+                           "algorithmic_bytes_per_launch": r["bytes_noncausal"],
+                           "counters": shader_counters("fwd_kernel<64, false> grid=%d" % (8 * 16 * 16 * 256))}
         log("forward", out["detail"])
 
     if "decode" in legs:

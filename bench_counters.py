@@ -14,7 +14,7 @@
     rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA SQ_INSTS_VALU \
         SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d OUT/sq -o run -- \
         python3 <repo>/bench.py --legs fwd,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3
-    python3 <repo>/bench_counters.py sq OUT/sq        # -> profiles/sq_counters.md
+    python3 <repo>/bench_counters.py sq OUT/sq        # -> profiles/sq_counters.md and .json
     # kernel durations of a plain bench run:
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- python3 <repo>/bench.py
     python3 <repo>/bench_counters.py trace OUT/trace  # -> profiles/kernel_trace.md
@@ -104,15 +104,19 @@ def sq_summary(run_dir: str, cmd: str) -> str:
              "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS." % (XCDS, SIMDS), "",
              "| kernel | GPU cycles | MFMA busy % | VALU active % | MFMA instr | VALU instr | LDS instr | LDS bank conflicts | conflicts / LDS instr |",
              "|---|---|---|---|---|---|---|---|---|"]
+    table = {}
     for key in sorted(per):
         avg = {n: (sum(per[key][n].values()) / len(per[key][n])) if per[key][n] else float("nan") for n in names}
         gpu = avg["GRBM_GUI_ACTIVE"] / XCDS
+        table[key] = {"gpu_cycles": round(gpu), "mfma_busy_pct": round(100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS), 2)
+                      if gpu else None, "lds_instr": round(avg["SQ_INSTS_LDS"]),
+                      "lds_bank_conflicts": round(avg["SQ_LDS_BANK_CONFLICT"])}
         lines.append("| %s | %.0f | %.1f | %.1f | %.0f | %.0f | %.0f | %.0f | %.4f |" % (
             key, gpu, 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS) if gpu else float("nan"),
             100.0 * avg["SQ_ACTIVE_INST_VALU"] / avg["SQ_WAVE_CYCLES"] if avg["SQ_WAVE_CYCLES"] else float("nan"),
             avg["SQ_INSTS_MFMA"], avg["SQ_INSTS_VALU"], avg["SQ_INSTS_LDS"], avg["SQ_LDS_BANK_CONFLICT"],
             avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_INSTS_LDS"] if avg["SQ_INSTS_LDS"] else float("nan")))
-    return "\n".join(lines) + "\n"
+    return "\n".join(lines) + "\n", table
 
 
 def trace_summary(run_dir: str, cmd: str, tail: int = 200) -> str:
@@ -160,9 +164,13 @@ def main():
         cmd = ("rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA SQ_INSTS_VALU "
                "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d OUT/sq -o run -- "
                "python3 <repo>/bench.py --legs fwd,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3")
-        text = sq_summary(args[1], cmd)
+        text, table = sq_summary(args[1], cmd)
         with open(os.path.join(ROOT, "profiles", "sq_counters.md"), "w") as f:
             f.write(text)
+        import bench
+
+        with open(os.path.join(ROOT, "profiles", "sq_counters.json"), "w") as f:
+            json.dump({"kernel_source_hash": bench.kernel_source_hash(), "command": cmd, "kernels": table}, f, indent=1)
         print(text)
         return
     if len(args) == 2 and "=" not in args[0]:
