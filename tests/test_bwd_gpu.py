@@ -85,7 +85,7 @@ def test_bwd_is_deterministic():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, True)])
+@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, False), (128, True)])
 def test_bwd_training_shape_sampled(orc, d, causal):
     """B=16, H=16, N=1024 (the prefill workload) checked on four whole (b, h) slices: a
     slice's gradients depend on that slice only, so the oracle runs on the slices alone."""
@@ -100,3 +100,21 @@ def test_bwd_training_shape_sampled(orc, d, causal):
         sl = (slice(b, b + 1), slice(h, h + 1))
         dQ, dK, dV, _ = orc.attention_bwd(Q[sl], K[sl], V[sl], dO[sl], causal=causal, scale=scale)
         check_grads("%s slice b=%d h=%d" % (name, b, h), (dq[sl], dk[sl], dv[sl]), (dQ, dK, dV))
+
+
+def test_bwd_gqa_ragged_sampled(orc):
+    """B=4, H=32 query heads over H_kv=8 key/value heads, N=4095 (a ragged last tile), d=128,
+    causal, checked on whole key/value groups: a group's gradients (its four query heads' dQ,
+    its dK and dV) depend on that group only, so the oracle runs on the group alone."""
+    B, H, H_kv, N, d = 4, 32, 8, 4095, 128
+    name = "bwd GQA ragged B=4 H=32/8 N=4095 d=128 causal"
+    say(name)
+    scale = scale_for(d)
+    Q, K, V, dO = case(29, B, H, H_kv, N, N, d, True)
+    dq, dk, dv = run(Q, K, V, dO, True, scale)
+    dq, dk, dv = bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)
+    G = H // H_kv
+    for b, g in ((0, 0), (3, 5)):
+        qs, ks = (slice(b, b + 1), slice(g * G, g * G + G)), (slice(b, b + 1), slice(g, g + 1))
+        dQ, dK, dV, _ = orc.attention_bwd(Q[qs], K[ks], V[ks], dO[qs], causal=True, scale=scale)
+        check_grads("%s group b=%d g=%d" % (name, b, g), (dq[qs], dk[ks], dv[ks]), (dQ, dK, dV))
