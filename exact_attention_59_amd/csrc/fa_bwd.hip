@@ -155,8 +155,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
     int bh, rank;
-    map_block_xcd(blockIdx.x, T_r, BH, bh, rank);
-    const int q_tile = CAUSAL ? T_r - 1 - rank : rank;  // causal: long tiles dispatch first
+    // Under the causal mask a workgroup takes the pair of query tiles (T_r-1-rank, rank), so
+    // that every workgroup carries the same work (no tail of long tiles).
+    const int n_ranks = CAUSAL ? (T_r + 1) / 2 : T_r;
+    map_block_xcd(blockIdx.x, n_ranks, BH, bh, rank);
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / H_kv);
     const int64_t q_base = (int64_t)bh * N_q * D;
@@ -164,6 +166,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
     const int off = N_k - N_q;
     const int T_c = (N_k + BC - 1) / BC;
 
+  auto run = [&](const int q_tile) {
     const int q0w = q_tile * BR + w * 32, q_row = q0w + l32;
     int n_tiles = T_c, n_w = T_c;  // tiles the workgroup stages / this wave computes
     {
@@ -264,6 +267,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
                           pack_bf16x2(acc[db][4 * gq + 2] * scale, acc[db][4 * gq + 3] * scale)};
             }
     }
+  };
+
+    run(CAUSAL ? T_r - 1 - rank : rank);
+    if (CAUSAL && rank != T_r - 1 - rank) {
+        __syncthreads();  // the first tile's last LDS reads are done before the next prologue
+        run(rank);
+    }
 }
 
 // ---------------------------------------------------------------------------- dK, dV
@@ -292,12 +302,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
-    int bg, kt;
-    map_block_xcd(blockIdx.x, T_k, BG, bg, kt);
+    // Under the causal mask a workgroup takes the pair of key tiles (kr, T_k-1-kr): early keys
+    // are seen by many query tiles, late ones by few, and the pair evens the work out.
+    int bg, kr;
+    const int n_ranks = CAUSAL ? (T_k + 1) / 2 : T_k;
+    map_block_xcd(blockIdx.x, n_ranks, BG, bg, kr);
     const int b = bg / H_kv, g = bg - b * H_kv;
     const int group = H / H_kv;
     const int64_t kv_base = (int64_t)bg * N_k * D;
     const int off = N_k - N_q;
+  auto run = [&](const int kt) {
     const int k0w = kt * BK + w * 32, key = k0w + l32;
 
     // Query tiles that can see a key of this workgroup (query q sees key k iff k <= q + off).
@@ -417,6 +431,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
             }
         }
     }
+  };
+
+    run(kr);
+    if (CAUSAL && kr != T_k - 1 - kr) {
+        __syncthreads();  // the first tile's last LDS reads are done before the next prologue
+        run(T_k - 1 - kr);
+    }
 }
 
 // ---------------------------------------------------------------------------- dK, dV (wave pairs)
@@ -447,12 +468,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const int pr = w & 3;
     const bool ds_wave = w >= 4;
     const int l32 = lane & 31, hh = lane >> 5;
-    int bg, kt;
-    map_block_xcd(blockIdx.x, T_k, BG, bg, kt);
+    // Under the causal mask a workgroup takes the pair of key tiles (kr, T_k-1-kr): early keys
+    // are seen by many query tiles, late ones by few, and the pair evens the work out.
+    int bg, kr;
+    const int n_ranks = CAUSAL ? (T_k + 1) / 2 : T_k;
+    map_block_xcd(blockIdx.x, n_ranks, BG, bg, kr);
     const int b = bg / H_kv, g = bg - b * H_kv;
     const int group = H / H_kv;
     const int64_t kv_base = (int64_t)bg * N_k * D;
     const int off = N_k - N_q;
+  auto run = [&](const int kt) {
     const int k0w = kt * BK + pr * 32, key = k0w + l32;
 
     const int n_qt = (N_q + BQ - 1) / BQ;
@@ -584,6 +609,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
             for (int db = 0; db < D / 32; ++db) op[32 * db] = (uint16_t)(pack_bf16x2(acc[db][r] * f, 0.f) & 0xffffu);
         }
     }
+  };
+
+    run(kr);
+    if (CAUSAL && kr != T_k - 1 - kr) {
+        __syncthreads();  // the first tile's last LDS reads are done before the next prologue
+        run(T_k - 1 - kr);
+    }
 }
 
 template <int D, bool CAUSAL>
@@ -598,23 +630,25 @@ hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int T_r = (N_q + kBwdBlockRows - 1) / kBwdBlockRows;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)T_r * B * H)), dim3(256), 0, stream,
+    const int n_qr = CAUSAL ? (T_r + 1) / 2 : T_r;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qr * B * H)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                        static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(dO), LSE, Dv,
                        static_cast<uint16_t*>(dQ), H, H_kv, N_q, N_k, T_r, B * H, c, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int T_k = (N_k + kBwdBlockKeys - 1) / kBwdBlockKeys;
+    const int n_kr = CAUSAL ? (T_k + 1) / 2 : T_k;
     // d = 128: the wave-pair kernel (one wave cannot hold both accumulators and both
     // operand sets); d = 64: the single-wave kernel (measured 4% faster, same results).
     if constexpr (D == 128)
-        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)T_k * B * H_kv)), dim3(512), 0,
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_kr * B * H_kv)), dim3(512), 0,
                            stream, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                            static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(dO), LSE, Dv,
                            static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), H, H_kv, N_q, N_k, T_k, B * H_kv, c,
                            scale);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)T_k * B * H_kv)), dim3(256), 0,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_kr * B * H_kv)), dim3(256), 0,
                            stream, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                            static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(dO), LSE, Dv,
                            static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), H, H_kv, N_q, N_k, T_k, B * H_kv, c,
