@@ -280,10 +280,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
 // One workgroup of 4 waves per (b, key/value head, 128 keys); wave w owns 32 keys, lane =
 // key.  K and V rows of the wave sit in registers as B operands (used at d = 64; at d = 128
 // they and the two accumulators do not fit one wave: see bwd_dkdv_pair_kernel).  The
-// workgroup walks the 32-query tiles of every query head of the group.  Per tile: S = Q K^T and dP = dO V^T (A = Q, dO rows), P = 2^(c S -
-// L2), dS = P (dP - D); then dV += P^T dO and dK += dS^T Q, with P^T and dS^T already in
-// A-operand layout (the query index of the contraction permuted to match) and dO, Q as B
-// operands through transposing reads of the same tiles.
+// workgroup walks the queries of every query head of the group, staging 64 query rows of Q
+// and dO per barrier and computing them as two 32-row halves (one barrier and one round of
+// copies per 64 rows instead of per 32).  Per half: S = Q K^T and dP = dO V^T (A = Q, dO
+// rows), P = 2^(c S - L2), dS = P (dP - D); then dV += P^T dO and dK += dS^T Q, with P^T and
+// dS^T already in A-operand layout (the query index of the contraction permuted to match)
+// and dO, Q as B operands through transposing reads of the same tiles.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -291,12 +293,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H,
                                                           int H_kv, int N_q, int N_k, int T_k, int BG, float c,
                                                           float scale) {
-    constexpr int BK = kBwdBlockKeys, BQ = kBwdBlockQueries, QT = BQ * D;
+    constexpr int BK = kBwdBlockKeys, BQ = kBwdBlockQueries, SUB = 2, SQ = SUB * BQ, QT = SQ * D;
     __shared__ __attribute__((aligned(1024))) uint16_t q_s0[QT];
     __shared__ __attribute__((aligned(1024))) uint16_t q_s1[QT];
     __shared__ __attribute__((aligned(1024))) uint16_t o_s0[QT];  // dO
     __shared__ __attribute__((aligned(1024))) uint16_t o_s1[QT];
-    __shared__ __attribute__((aligned(16))) float ld_s[2][2 * BQ];  // [buffer][L2 of the tile's rows, then D]
+    __shared__ __attribute__((aligned(16))) float ld_s[2][2 * SQ];  // [buffer][L2 of the tile's rows, then D]
     asm volatile("" ::"s"(dK), "s"(dV));
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -315,8 +317,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     const int k0w = kt * BK + w * 32, key = k0w + l32;
 
     // Query tiles that can see a key of this workgroup (query q sees key k iff k <= q + off).
-    const int n_qt = (N_q + BQ - 1) / BQ;
-    const int qt0 = CAUSAL ? min(n_qt, max(0, kt * BK - off) / BQ) : 0;
+    const int n_qt = (N_q + SQ - 1) / SQ;
+    const int qt0 = CAUSAL ? min(n_qt, max(0, kt * BK - off) / SQ) : 0;
     const int per_head = n_qt - qt0;
     const int n_steps = group * per_head;
 
@@ -331,18 +333,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
 
     // Step s -> query head and tile.
     auto head_of = [&](int s) { return g * group + s / per_head; };
-    auto q0_of = [&](int s) { return (qt0 + s % per_head) * BQ; };
+    auto q0_of = [&](int s) { return (qt0 + s % per_head) * SQ; };
     auto stage = [&](int s, uint16_t* qs, uint16_t* os) {
         const int64_t base = ((int64_t)b * H + head_of(s)) * N_q * D;
         const int q0 = q0_of(s);
-        stage_tile<D, BQ>(Q + base, q0, N_q, qs, w, lane);
-        stage_tile<D, BQ>(dO + base, q0, N_q, os, w, lane);
+        stage_tile<D, SQ>(Q + base, q0, N_q, qs, w, lane);
+        stage_tile<D, SQ>(dO + base, q0, N_q, os, w, lane);
     };
     // Row constants of a tile (wave 0: lanes 0..31 L2 of rows q0 + lane, lanes 32..63 D),
     // loaded at the start of a step and stored to LDS at its end.
     auto load_ld = [&](int s) -> float {
         const int64_t rb = ((int64_t)b * H + head_of(s)) * N_q;
-        const int q = q0_of(s) + l32;
+        const int q = q0_of(s) + 32 * w + l32;
         if (q >= N_q) return hh == 0 ? INFINITY : 0.f;  // rows past N_q: P = 0
         if (hh == 0) {
             const float lse = LSE[rb + q];
@@ -350,8 +352,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         }
         return Dv[rb + q];
     };
-    auto compute = [&](int s, const uint16_t* qs, const uint16_t* os, const float* lds_ld) {
-        const int q0 = q0_of(s);
+    auto compute_sub = [&](int q0, const uint16_t* qs, const uint16_t* os, const float* l2p, const float* ddp) {
         if (CAUSAL && q0 + BQ - 1 + off < k0w) return;  // no row of the tile sees a key of this wave
         f32x16 st = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -370,9 +371,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
             for (int e = 0; e < 8; ++e) {
                 const int r = 8 * t + e;
                 const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                p[e] = exp2_hw(fmaf(st[r], c, -lds_ld[qr]));
+                p[e] = exp2_hw(fmaf(st[r], c, -l2p[qr]));
                 if (edge && key > q0 + qr + off) p[e] = 0.f;
-                ds[e] = p[e] * (dp[r] - lds_ld[BQ + qr]);
+                ds[e] = p[e] * (dp[r] - ddp[qr]);
             }
             pa[t] = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                     pack_bf16x2(p[6], p[7])});
@@ -388,10 +389,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
                 accK[db] = mfma32(dsa[t], tr_frag<D>(qs, o, db, t), accK[db]);
             }
     };
+    auto compute = [&](int s, const uint16_t* qs, const uint16_t* os, const float* lds_ld) {
+#pragma unroll
+        for (int h = 0; h < SUB; ++h)
+            compute_sub(q0_of(s) + BQ * h, qs + BQ * h * D, os + BQ * h * D, lds_ld + BQ * h, lds_ld + SQ + BQ * h);
+    };
+    const int ld_slot = (lane >> 5) * SQ + 32 * w + (lane & 31);  // waves 0..SUB-1 load row constants
 
     if (n_steps > 0) {
         stage(0, q_s0, o_s0);
-        if (w == 0) ld_s[0][lane] = load_ld(0);
+        if (w < SUB) ld_s[0][ld_slot] = load_ld(0);
     }
     wait_vmem();
     __syncthreads();
@@ -399,19 +406,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         float nxt = 0.f;
         if (s + 1 < n_steps) {
             stage(s + 1, q_s1, o_s1);
-            if (w == 0) nxt = load_ld(s + 1);
+            if (w < SUB) nxt = load_ld(s + 1);
         }
         compute(s, q_s0, o_s0, ld_s[0]);
-        if (w == 0 && s + 1 < n_steps) ld_s[1][lane] = nxt;
+        if (w < SUB && s + 1 < n_steps) ld_s[1][ld_slot] = nxt;
         wait_vmem();
         __syncthreads();
         if (s + 1 >= n_steps) break;
         if (s + 2 < n_steps) {
             stage(s + 2, q_s0, o_s0);
-            if (w == 0) nxt = load_ld(s + 2);
+            if (w < SUB) nxt = load_ld(s + 2);
         }
         compute(s + 1, q_s1, o_s1, ld_s[1]);
-        if (w == 0 && s + 2 < n_steps) ld_s[0][lane] = nxt;
+        if (w < SUB && s + 2 < n_steps) ld_s[0][ld_slot] = nxt;
         wait_vmem();
         __syncthreads();
     }
