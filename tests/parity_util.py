@@ -61,6 +61,32 @@ def fwd_inputs(seed, B, H, H_kv, N_q, N_k, d, f32_draw=False):
     return Q, K, V, raw
 
 
+def key_scale(pattern, N_k):
+    """Per-key factor of a score-range stress pattern.
+
+    ramp_up: the row maximum keeps growing along the keys, by more than any fixed slack
+    per 64 keys; ramp_down: the first keys dominate and later ones never raise it;
+    alternating: blocks of 64 keys switch between large and small scores."""
+    j = np.arange(N_k, dtype=np.float64)
+    if pattern == "ramp_up":
+        return 0.2 + 3.0 * j / max(1, N_k - 1)
+    if pattern == "ramp_down":
+        return 3.2 - 3.0 * j / max(1, N_k - 1)
+    if pattern == "alternating":
+        return np.where((j // 64) % 2 == 1, 3.0, 0.3)
+    raise ValueError(pattern)
+
+
+def stress_inputs(seed, B, H, H_kv, N_q, N_k, d, pattern, q_scale=4.0):
+    """bf16 Q/K/V whose scaled scores span tens of units: Q ~ N(0, q_scale^2), key j's row
+    ~ N(0, key_scale(pattern)[j]^2), rounded to bf16 after scaling."""
+    Q = gen.normal_bf16(seed, gen.TENSOR_Q, (B, H, N_q, d), q_scale)
+    Kf = gen.normal_f32(seed, gen.TENSOR_K, (B, H_kv, N_k, d))
+    K = gen.f32_to_bf16((Kf * key_scale(pattern, N_k)[None, None, :, None]).astype(np.float32))
+    V = gen.normal_bf16(seed, gen.TENSOR_V, (B, H_kv, N_k, d))
+    return Q, K, V
+
+
 def decode_inputs(seed, B, H, H_kv, N_k, d, q_scale=3.0):
     Q = gen.normal_bf16(seed, gen.TENSOR_Q, (B, H, 1, d), q_scale)
     K = gen.normal_bf16(seed, gen.TENSOR_K, (B, H_kv, N_k, d))
@@ -115,10 +141,15 @@ def check(name, O_gpu, O_ref, L_gpu, L_ref):
     return res
 
 
-def check_grads(name, gpu, ref):
-    """Apply the gradient gates to (dQ, dK, dV); returns the errors relative to m and a."""
+def check_grads(name, gpu, ref, allow=None):
+    """Apply the gradient gates to (dQ, dK, dV); returns the errors relative to m and a.
+
+    allow: optional per-element allowances (arrays shaped like the gradients, or None) for
+    error that an input carries in, e.g. o_rounding_allowance; each element's error is
+    reduced by its allowance (not below zero) before the gates."""
     out = {}
-    for label, g, r in zip(("dQ", "dK", "dV"), gpu, ref):
+    allow = allow or (None, None, None)
+    for label, g, r, al in zip(("dQ", "dK", "dV"), gpu, ref, allow):
         g = np.asarray(g, dtype=np.float64)
         r = np.asarray(r, dtype=np.float64)
         assert g.shape == r.shape, "%s %s: shape %s vs %s" % (name, label, g.shape, r.shape)
@@ -126,12 +157,46 @@ def check_grads(name, gpu, ref):
         m = max(float(np.abs(r).max()), G_FLOOR)
         a = max(float(np.abs(r).mean()), G_FLOOR)
         err = np.abs(g - r)
+        if al is not None:
+            err = np.maximum(err - np.abs(al), 0.0)
         out[label] = (float(err.max()) / m, float(err.mean()) / a, m)
     say(name, {k: "max %.2e m, mean %.2e a (m %.3g)" % v for k, v in out.items()})
     for label, (mx, mn, _) in out.items():
         assert mx <= G_MAX, "%s: %s max-abs %.3g m > %.3g m" % (name, label, mx, G_MAX)
         assert mn <= G_MEAN, "%s: %s mean-abs %.3g a > %.3g a" % (name, label, mn, G_MEAN)
     return out
+
+
+def o_rounding_allowance(Q, K, dO, O_ref, O_bf16, L_ref, scale, causal):
+    """First-order effect on (dQ, dK) of the O handed to the backward being O_bf16 (the bf16
+    rounding of the exact O) instead of O itself.
+
+    The backward's row term D_i = dO_i . O_i is taken from the stored O, so its rounding
+    enters dS = P o (dP - D) as -P_ij dD_i with dD_i = dO_i . (O_bf16 - O)_i, giving
+    dQ_i += -scale dD_i (P K)_i and dK_j += -scale sum_i P_ij dD_i Q_i.  In rows whose
+    softmax is sharply peaked, dQ_i itself nearly cancels while this term does not, so it can
+    exceed the gates that bound the backward's own rounding.  Inputs as the oracle takes
+    them (uint16 bf16 bits for Q, K, dO, O_bf16; float64 O_ref, L_ref); P is rebuilt here
+    from the oracle's L_ref.  Returns (allow_dQ, allow_dK, None)."""
+    q = gen.bf16_to_f32(Q).astype(np.float64)
+    k = gen.bf16_to_f32(K).astype(np.float64)
+    do = gen.bf16_to_f32(dO).astype(np.float64)
+    ob = gen.bf16_to_f32(O_bf16).astype(np.float64)
+    B, H, N_q, d = q.shape
+    H_kv, N_k = k.shape[1], k.shape[2]
+    g = H // H_kv
+    kk = np.repeat(k, g, axis=1)
+    s = np.einsum("bhqd,bhkd->bhqk", q, kk) * scale
+    if causal:
+        hidden = np.arange(N_k)[None, :] > (np.arange(N_q)[:, None] + (N_k - N_q))
+        s = np.where(hidden, -np.inf, s)
+    finite = np.isfinite(L_ref)
+    P = np.where(finite[..., None], np.exp(s - np.where(finite, L_ref, 0.0)[..., None]), 0.0)
+    dD = (do * (ob - O_ref)).sum(-1)
+    dQ = -scale * dD[..., None] * np.einsum("bhqk,bhkd->bhqd", P, kk)
+    dK = -scale * np.einsum("bhqk,bhqd->bhkd", P, dD[..., None] * q)
+    dK = dK.reshape(B, H_kv, g, N_k, d).sum(2)
+    return dQ, dK, None
 
 
 def check_fp8(name, O_gpu, O_q, L_gpu, L_q, O_x=None, L_x=None, lse_slack=None):

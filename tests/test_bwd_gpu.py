@@ -9,7 +9,8 @@ import pytest
 
 import gen
 import oracle
-from parity_util import bf16_dev_to_f64, check_grads, fwd_inputs, say, scale_for, to_dev
+from parity_util import (bf16_dev_to_f64, check_grads, fwd_inputs, o_rounding_allowance, say, scale_for,
+                         stress_inputs, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +73,31 @@ def test_bwd_small(orc, B, H, H_kv, N_q, N_k, d, causal):
     check_grads(name, (bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)), (dQ, dK, dV))
     if causal and N_q > N_k:  # rows that see no key get exactly zero
         assert np.all(bf16_dev_to_f64(dq)[:, :, :N_q - N_k] == 0.0), name
+
+
+@pytest.mark.parametrize("pattern", ["ramp_up", "alternating"])
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_bwd_score_range_stress(orc, pattern, d, causal):
+    """P recomputed from the saved LSE when scores span tens of units (peaked rows).
+
+    The backward is fed the oracle's O (rounded to bf16, as a forward stores it) and LSE, so
+    that the allowance for O's rounding (o_rounding_allowance) is computed from oracle values
+    only; the gates then bound the backward's own arithmetic."""
+    B, H, H_kv, N_q, N_k = 1, 4, 2, 300, 520
+    name = "bwd stress %s d=%d causal=%s" % (pattern, d, causal)
+    say(name)
+    scale = scale_for(d)
+    Q, K, V = stress_inputs(900 + d, B, H, H_kv, N_q, N_k, d, pattern)
+    dO = gen.normal_bf16(900 + d, gen.TENSOR_DO, (B, H, N_q, d))
+    O_ref, L_ref = orc.attention(Q, K, V, causal=causal, scale=scale)
+    O_b = gen.f32_to_bf16(O_ref.astype(np.float32))
+    q, k, v, do, o = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO), to_dev(O_b)
+    lse = torch.from_numpy(L_ref.astype(np.float32)).to("cuda:0")
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    dQ, dK, dV, _ = orc.attention_bwd(Q, K, V, dO, causal=causal, scale=scale)
+    allow = o_rounding_allowance(Q, K, dO, O_ref, O_b, L_ref, scale, causal)
+    check_grads(name, (bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)), (dQ, dK, dV), allow)
 
 
 def test_bwd_is_deterministic():

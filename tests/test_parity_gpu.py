@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity_util import (bf16_dev_to_f64, check, decode_inputs, fwd_inputs, sample_rows, say, scale_for,
-                         to_dev)
+from parity_util import (bf16_dev_to_f64, check, decode_inputs, fwd_inputs, key_scale, sample_rows, say,
+                         scale_for, stress_inputs, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +93,32 @@ def test_fwd_exact_cases(orc, d):
     O_ref, L_ref = orc.attention(Q, K, V)
     check("fwd Q=0 d=%d" % d, bf16_dev_to_f64(o), O_ref, lse.cpu().numpy(), L_ref)
     assert np.max(np.abs(lse.cpu().numpy() - math.log(150))) <= 1e-5
+
+
+STRESS = [
+    # B, H, H_kv, N_q, N_k, d, causal
+    (1, 4, 2, 300, 700, 64, False),
+    (1, 4, 2, 300, 700, 64, True),
+    (2, 2, 1, 257, 513, 128, True),
+    (1, 2, 2, 200, 1000, 128, False),
+]
+
+
+@pytest.mark.parametrize("pattern", ["ramp_up", "ramp_down", "alternating"])
+@pytest.mark.parametrize("B,H,H_kv,N_q,N_k,d,causal", STRESS)
+def test_fwd_score_range_stress(orc, pattern, B, H, H_kv, N_q, N_k, d, causal):
+    """Scores spanning tens of units whose row maximum jumps many times along the keys (the
+    running max and the rescale of acc and l, including factors that underflow to zero),
+    never moves after the first keys, or alternates between key blocks."""
+    name = "fwd stress %s %s" % (pattern, str((B, H, H_kv, N_q, N_k, d, causal)))
+    say(name)
+    Q, K, V = stress_inputs(500 + N_k + d, B, H, H_kv, N_q, N_k, d, pattern)
+    o, lse = run_fwd(Q, K, V, causal)
+    O_ref, L_ref = orc.attention(Q, K, V, causal=causal)
+    # the inputs do stress the range: scaled scores of a row spread over more than 8 log2 units
+    spread = (L_ref.max() - L_ref.min()) / math.log(2)
+    assert spread > 8.0, spread
+    check(name, bf16_dev_to_f64(o), O_ref, lse.cpu().numpy(), L_ref)
 
 
 def test_fwd_scale_and_determinism(orc):
