@@ -248,6 +248,22 @@ def test_decode_small(orc, B, H, H_kv, N_k, d, S):
     check(name + " combined", bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
 
 
+@pytest.mark.parametrize("pattern", ["ramp_up", "ramp_down", "alternating"])
+@pytest.mark.parametrize("B,H,H_kv,N_k,d,S", [(2, 8, 2, 3000, 128, 7), (1, 4, 1, 1500, 64, 24)])
+def test_decode_score_range_stress(orc, pattern, B, H, H_kv, N_k, d, S):
+    """Segments whose log-sum-exps differ by tens of units: the merge weights e^(lse_s - lse)
+    span many orders of magnitude (ramp_up: the last segment dominates; ramp_down: the first)."""
+    name = "decode stress %s %s" % (pattern, str((B, H, H_kv, N_k, d, S)))
+    say(name)
+    Q, K, V = stress_inputs(3000 + N_k + S, B, H, H_kv, 1, N_k, d, pattern)
+    o_part, l_part, o, l = run_decode(Q, K, V, S)
+    check_segments(orc, name, Q, K, V, S, o_part, l_part)
+    O_ref, L_ref = orc.attention(Q, K, V)
+    check(name + " combined", bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
+    lp = l_part.cpu().numpy()
+    assert float((lp.max(-1) - lp.min(-1)).max()) > 10.0  # the segments' LSEs do spread
+
+
 @pytest.mark.parametrize("N_k,seed", [(4096, 5), (65536, 6)])
 def test_decode_full_workloads(orc, N_k, seed):
     B, H, H_kv, d = 4, 32, 8, 128
