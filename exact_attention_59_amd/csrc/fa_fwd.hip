@@ -70,10 +70,11 @@ __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 
 // whatever m is used, it cancels between the numerator acc and the denominator l.
 constexpr float kRescaleSlack = 8.0f;
 
-// Two workgroups (8 waves) per CU.  (Three fit at d = 64 but measured no faster: the
-// loop is bound by LDS read throughput, not by latency.)
+// Workgroups per CU: three at d = 64 (at most 168 VGPRs, 12 waves per CU), whose third
+// wave per SIMD covers latency that two leave exposed; two at d = 128 (its MFMA tiles and
+// accumulators need up to 256 VGPRs).
 template <int D>
-constexpr int kFwdBlocksPerCU = 2;
+constexpr int kFwdBlocksPerCU = D == 64 ? 3 : 2;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint16_t* __restrict__ Q,
@@ -322,16 +323,16 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
             KFrag kf;
             VFrag vf;
             if constexpr (D == 64) {
-                // All fragments of K_{j+1} and V_j^T are requested before any arithmetic,
-                // so their latency overlaps the softmax instead of stalling each MFMA.
-                load_k(k_read, kf);
-                load_v(v_read, vf, std::integral_constant<int, 0>{}, std::integral_constant<int, BC / 16>{});
-                __builtin_amdgcn_sched_barrier(0);
+                // K_{j+1} fragments are read once the max is known and V_j^T fragments
+                // before the exps, so that few fragments are live at once (the register
+                // budget of three workgroups per CU) and V's read latency overlaps the exps.
                 const float m_use = softmax_prepare(s_cur, j);
+                load_k(k_read, kf);
                 // Tile j+1's scores, issued unconditionally so that the MFMAs share a basic
                 // block with the exps below and overlap them.  Past this wave's last tile the
                 // buffer holds other finite data and the result is never used.
                 qk(kf, s_next);
+                load_v(v_read, vf, std::integral_constant<int, 0>{}, std::integral_constant<int, BC / 16>{});
                 softmax_finish(s_cur, m_use, pf);
                 pv(vf, pf);
             } else {
