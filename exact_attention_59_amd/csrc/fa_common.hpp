@@ -141,6 +141,11 @@ __device__ __forceinline__ void wave_lds_fence() {
 __device__ __forceinline__ void copy_to_lds16(const void* g, uint32_t lds_base) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
+// The same copy with a wave-uniform base address (SGPR pair) and a 32-bit per-lane byte
+// offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void copy_to_lds16_sbase(const void* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_base) : "memory");
+}
 
 // s_waitcnt vmcnt(0): this wave's global->LDS copies have landed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
