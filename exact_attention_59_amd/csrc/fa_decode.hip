@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
     constexpr int KB = C::KB, NQ = C::NQ, NW = C::NW, CPR = C::CPR;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM_BYTES];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
     const int n16 = lane & 15, hq = lane >> 4;
 
     int bid = blockIdx.x;
@@ -100,23 +101,29 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
     const bool q_valid = qh < group;
     const int h = g * group + qh;
 
-    // Q fragment (B operand): lane holds Q[h][32*t + 8*hq + e] for step t.
-    bf16x8 qf[C::KSTEPS];
-    if (q_valid) {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(Q + ((int64_t)b * H + h) * D + 8 * hq);
+    // Q fragment (B operand): lane holds Q[h][32*t + 8*hq + e] for step t.  The loads are
+    // issued here and their values taken (through the opaque copy) only once the first
+    // K/V blocks' loads are in flight as well, so that no wave waits on Q alone.
+    // Columns past the group read the group's last head (finite values; their outputs are
+    // never stored), so that the loads are unconditional like the K/V loads below.
+    u32x4 q_raw[C::KSTEPS];
+    {
+        const int h_ld = q_valid ? h : g * group + group - 1;
+        const u32x4* qp = reinterpret_cast<const u32x4*>(Q + ((int64_t)b * H + h_ld) * D + 8 * hq);
 #pragma unroll
-        for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(vgpr_copy(qp[4 * t]));
-    } else {
-#pragma unroll
-        for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(u32x4{0, 0, 0, 0});
+        for (int t = 0; t < C::KSTEPS; ++t) q_raw[t] = qp[4 * t];
     }
+    bf16x8 qf[C::KSTEPS];
 
     uint16_t* Vs = reinterpret_cast<uint16_t*>(smem) + w * C::V_ELEMS;
 
     // ---- block loads.  K: lane (n16, hq) holds row 16*mb + n16, d = 32*t + 8*hq + 0..7
     // (the 4 lanes of a row cover one 64-byte line per instruction).  V: lane holds row
     // v_kg*V_LOADS + r, chunk v_dc (V_LOADS divides 16: a lane's rows share a 16-key half).
-    // Rows past the segment read as zero, from a clamped in-bounds address.
+    // Rows past the segment read the segment's last row again (a clamped in-bounds address,
+    // finite data): their scores are masked to -inf, so they get P = 0 and add nothing.
+    // The loads are unconditional (no zero fill), so that no wave waits on one block's
+    // loads before the next block's are requested.
     const int v_dc = lane % CPR, v_kg = lane / CPR;
     static_assert(16 % C::V_LOADS == 0, "a lane's V rows stay in one 16-key half");
     auto load_block = [&](int bi, u32x4 (&kr)[C::K_LOADS], u32x4 (&vr)[C::V_LOADS]) {
@@ -147,16 +154,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
             const int rel = (full ? key : min(key, k_end - 1)) - key0;  // in-bounds row
             const u32x4* kp = reinterpret_cast<const u32x4*>((rel >= 16 ? kh1 : kh0) + (rel & 15) * D + 8 * hq);
 #pragma unroll
-            for (int t = 0; t < C::KSTEPS; ++t)
-                kr[mb * C::KSTEPS + t] = (full || key < k_end) ? kp[4 * t] : u32x4{0, 0, 0, 0};
+            for (int t = 0; t < C::KSTEPS; ++t) kr[mb * C::KSTEPS + t] = kp[4 * t];
         }
 #pragma unroll
         for (int r = 0; r < C::V_LOADS; ++r) {
             const int key = key0 + v_kg * C::V_LOADS + r;
             const int rel = (full ? key : min(key, k_end - 1)) - key0;
-            vr[r] = (full || key < k_end)
-                        ? *reinterpret_cast<const u32x4*>((rel >= 16 ? vh1 : vh0) + (rel & 15) * D + v_dc * 8)
-                        : u32x4{0, 0, 0, 0};
+            vr[r] = *reinterpret_cast<const u32x4*>((rel >= 16 ? vh1 : vh0) + (rel & 15) * D + v_dc * 8);
         }
     };
 
@@ -178,7 +182,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
 
-    auto compute = [&](int bi, const u32x4 (&kr)[C::K_LOADS], const u32x4 (&vr)[C::V_LOADS],
+    // Block bi's keys at or past `lim` (the segment's end) are masked.
+    auto compute = [&](int bi, int lim, const u32x4 (&kr)[C::K_LOADS], const u32x4 (&vr)[C::V_LOADS],
                        auto&& refill) {
         // V block -> this wave's LDS (row-major, swizzled chunks)
 #pragma unroll
@@ -196,14 +201,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
         }
         refill();  // this block's K registers are consumed; V is in LDS
         wave_lds_fence();
-        // mask keys past the segment (only the last block can be short)
+        // mask keys past the segment (only the last block can be short) or the whole block
         const int key0 = k_beg + bi * KB;
-        if (key0 + KB > k_end) {
+        if (key0 + KB > lim) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (key0 + 16 * mb + 4 * hq + r >= k_end) sc[mb][r] = -INFINITY;
+                    if (key0 + 16 * mb + 4 * hq + r >= lim) sc[mb][r] = -INFINITY;
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -244,14 +249,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
     };
 
     // Two-slot register ring: while block i is computed, blocks i+NW and i+2*NW (this
-    // wave's next two) are in flight.
+    // wave's next two) are in flight.  Q's values are taken once the first two blocks'
+    // loads are issued as well.
     u32x4 k0[C::K_LOADS], v0[C::V_LOADS], k1[C::K_LOADS], v1[C::V_LOADS];
     if (w < nblk) load_block(w, k0, v0);
     if (w + NW < nblk) load_block(w + NW, k1, v1);
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t) qf[t] = as_bf16x8(vgpr_copy(q_raw[t]));
     for (int bi = w; bi < nblk; bi += 2 * NW) {
-        compute(bi, k0, v0, [&] { if (bi + 2 * NW < nblk) load_block(bi + 2 * NW, k0, v0); });
+        compute(bi, k_end, k0, v0, [&] { if (bi + 2 * NW < nblk) load_block(bi + 2 * NW, k0, v0); });
         if (bi + NW < nblk)
-            compute(bi + NW, k1, v1, [&] { if (bi + 3 * NW < nblk) load_block(bi + 3 * NW, k1, v1); });
+            compute(bi + NW, k_end, k1, v1, [&] { if (bi + 3 * NW < nblk) load_block(bi + 3 * NW, k1, v1); });
     }
 
     // Merge the 4 wave states through LDS (reusing the V blocks).
