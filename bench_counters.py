@@ -190,13 +190,18 @@ def main():
         fetch_per = read_counter(f_dir, "FETCH_SIZE", label, fetch_per)
         write_per = read_counter(w_dir, "WRITE_SIZE", label, write_per)
     fetch, write = averages(fetch_per), averages(write_per)
-    # The calibration copy is the 1 GiB one: the largest copy dispatch (other, small
-    # runtime copies of the bench's set-up also match the name).
-    copies = [k for k in fetch if k.startswith("copy") and k in write]
-    if not copies:
-        raise SystemExit("the copy kernel is missing from the runs (use --legs ...,copy)")
-    big = max(copies, key=lambda k: fetch[k])
-    fetch["copy"], write["copy"] = fetch[big], write[big]
+    # The calibration copy is the 1 GiB one.  Other copies of the bench's set-up (the decode
+    # leg's rotated cache copies, at most 537 MB each, share the copy kernel's grid; torch
+    # copy kernels also match the name) are smaller, so the calibration takes the copy
+    # dispatches within 1% of the largest one, per counter.
+    def largest_copies(per) -> float:
+        vals = [x for k, v in per.items() if k.startswith("copy") for x in v.values()]
+        if not vals:
+            raise SystemExit("the copy kernel is missing from the runs (use --legs ...,copy)")
+        top = [x for x in vals if x >= 0.99 * max(vals)]
+        return sum(top) / len(top)
+
+    fetch["copy"], write["copy"] = largest_copies(fetch_per), largest_copies(write_per)
     f_read = COPY_BYTES / (fetch["copy"] * 1024.0)
     f_write = COPY_BYTES / (write["copy"] * 1024.0)
     kernels = {}
