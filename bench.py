@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,decode] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,fwd_other,decode,...]
 
 One step = fa_fwd over the batched-prefill workload (B=16, H=16, N_q=N_k=1024, d=64,
 bf16), once without and once with the causal mask.  `value` is that step's nominal
 FLOPs (4*B*H*N_q*N_k*d, halved under the causal mask) over its GPU time, in TFLOPS.
+The other forward workloads (long-sequence causal B=2 H=16 N=8192 d=128, grouped-query
+ragged causal B=4 H=32/8 N=4095 d=128, and the batched-prefill shape at d=128) are
+reported under "also_measured".
 The flash-decoding leg (B=4, H=32, H_kv=8, d=128, N_k = 4096 and 65536; split kernel
 then combine kernel) runs in the same invocation and is reported under "decode" in
 GB/s of K+V read once, against the 8 TB/s HBM peak.  The split kernel's rate comes from
@@ -430,8 +433,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
-    ap.add_argument("--legs", default="fwd,decode,bwd,fp8,cpu", help="comma list of fwd, decode, bwd, fp8, cpu, copy")
-    ap.add_argument("--all", action="store_true", help="also time the long-sequence and GQA forward workloads")
+    ap.add_argument("--legs", default="fwd,fwd_other,decode,bwd,fp8,cpu",
+                    help="comma list of fwd, fwd_other (the long-sequence, GQA and d=128 forward workloads), "
+                         "decode, bwd, fp8, cpu, copy")
+    ap.add_argument("--all", action="store_true", help="add fwd_other to --legs")
     ap.add_argument("--decode-reps", type=int, default=30)
     ap.add_argument("--decode-nk", default="4096,65536", help="comma list of decode cache lengths")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -510,7 +515,7 @@ def main():
         log("fp8", out["fp8"])
         torch.cuda.empty_cache()
 
-    if args.all:
+    if args.all or "fwd_other" in legs:
         others = [("long causal B=2 H=16 N=8192 d=128", 3, 2, 16, 16, 8192, 128, True),
                   ("GQA ragged causal B=4 H=32 H_kv=8 N=4095 d=128", 4, 4, 32, 8, 4095, 128, True),
                   ("batched prefill B=16 H=16 N=1024 d=128 non-causal", 2, 16, 16, 16, 1024, 128, False)]
