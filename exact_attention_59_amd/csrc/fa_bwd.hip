@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
     // Under the causal mask a workgroup takes the pair of query tiles (T_r-1-rank, rank), so
     // that every workgroup carries the same work (no tail of long tiles).
     const int n_ranks = CAUSAL ? (T_r + 1) / 2 : T_r;
-    map_block_xcd(blockIdx.x, n_ranks, BH, bh, rank);
+    map_block_xcd(blockIdx.x, n_ranks, BH, H / H_kv, bh, rank);
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / H_kv);
     const int64_t q_base = (int64_t)bh * N_q * D;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     // are seen by many query tiles, late ones by few, and the pair evens the work out.
     int bg, kr;
     const int n_ranks = CAUSAL ? (T_k + 1) / 2 : T_k;
-    map_block_xcd(blockIdx.x, n_ranks, BG, bg, kr);
+    map_block_xcd(blockIdx.x, n_ranks, BG, 1, bg, kr);
     const int b = bg / H_kv, g = bg - b * H_kv;
     const int group = H / H_kv;
     const int64_t kv_base = (int64_t)bg * N_k * D;
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     // are seen by many query tiles, late ones by few, and the pair evens the work out.
     int bg, kr;
     const int n_ranks = CAUSAL ? (T_k + 1) / 2 : T_k;
-    map_block_xcd(blockIdx.x, n_ranks, BG, bg, kr);
+    map_block_xcd(blockIdx.x, n_ranks, BG, 1, bg, kr);
     const int b = bg / H_kv, g = bg - b * H_kv;
     const int group = H / H_kv;
     const int64_t kv_base = (int64_t)bg * N_k * D;

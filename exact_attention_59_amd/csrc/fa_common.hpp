@@ -58,16 +58,22 @@ __device__ __forceinline__ int pack_fp8x2(float a, float b, int old) {
 }
 
 // Workgroup id -> (head index, rank within the head).  Consecutive ids are dispatched
-// round-robin over the 8 XCDs, each with its own L2.  When the head count is a multiple of
-// 8, every workgroup of a head goes to the same XCD (id % 8 == head % 8) and, within an
-// XCD, ids walk head by head, so the workgroups of a head are resident together and share
-// the head's tiles in that L2.  Otherwise ids go rank-major over all heads.
-__device__ __forceinline__ void map_block_xcd(int bid, int n_ranks, int n_heads, int& head, int& rank) {
-    if ((n_heads & 7) == 0) {
+// round-robin over the 8 XCDs, each with its own L2.  Heads are numbered so that the `group`
+// consecutive heads that read one K/V head (grouped-query attention; group = 1 otherwise)
+// form a unit.  When the number of units is a multiple of 8, every workgroup of a unit goes
+// to the same XCD (id % 8 == unit % 8) and, within an XCD, ids walk head by head through
+// the unit, so the workgroups that read the same K/V tiles are resident together and share
+// them in that L2.  Otherwise, when the head count is a multiple of 8, heads are spread the
+// same way one by one; else ids go rank-major over all heads.
+__device__ __forceinline__ void map_block_xcd(int bid, int n_ranks, int n_heads, int group, int& head, int& rank) {
+    const int n_units = n_heads / group;
+    if ((n_units & 7) == 0 || (n_heads & 7) == 0) {
+        const int g = (n_units & 7) == 0 ? group : 1;
         const int xcd = bid & 7, li = bid >> 3;
-        const int hl = li / n_ranks;
+        const int hl = li / n_ranks;  // the XCD's hl-th head
         rank = li - hl * n_ranks;
-        head = xcd + 8 * hl;
+        const int unit = xcd + 8 * (hl / g);
+        head = unit * g + (hl - (hl / g) * g);
     } else {
         rank = bid / n_heads;
         head = bid - rank * n_heads;

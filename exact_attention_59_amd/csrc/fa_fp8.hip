@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     const int l32 = lane & 31, hh = lane >> 5;
     const int n_ranks = CAUSAL ? (T_r + 1) / 2 : T_r;
     int bh, rank;
-    map_block_xcd(blockIdx.x, n_ranks, BH, bh, rank);
+    map_block_xcd(blockIdx.x, n_ranks, BH, H / H_kv, bh, rank);
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / H_kv);
     const int bg = b * H_kv + g;

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     // query tiles (T_r-1-rank, rank): every workgroup then carries the same work.
     const int n_ranks = CAUSAL ? (T_r + 1) / 2 : T_r;
     int bh, rank;
-    map_block_xcd(blockIdx.x, n_ranks, BH, bh, rank);
+    map_block_xcd(blockIdx.x, n_ranks, BH, H / H_kv, bh, rank);
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / H_kv);
     const int64_t q_base = (int64_t)bh * N_q * D;
