@@ -97,16 +97,24 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, const Offsets<D>
     return __builtin_bit_cast(bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
-// Load the B operand fragments of a row (q . k along d): lane holds row[16*ks + 8*hh + e].
+// The B operand fragments of a row (q . k along d): lane holds row[16*ks + 8*hh + e].
+// Loading takes two calls, so that several rows' loads (and a prologue's tile copies) are in
+// flight before the wave waits for any of them: issue_row_loads reads a row that must be
+// readable (callers clamp the index; no branch), take_row_frags takes the values through
+// the opaque copy once they are needed and zeroes those of a row that is not valid.
 template <int D>
-__device__ __forceinline__ void load_row_frags(const uint16_t* row, bool valid, int hh, bf16x8 (&f)[D / 16]) {
-    if (valid) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + 8 * hh);
+__device__ __forceinline__ void issue_row_loads(const uint16_t* row, int hh, u32x4 (&raw)[D / 16]) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row + 8 * hh);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) f[ks] = as_bf16x8(vgpr_copy(p[2 * ks]));
-    } else {
+    for (int ks = 0; ks < D / 16; ++ks) raw[ks] = p[2 * ks];
+}
+template <int D>
+__device__ __forceinline__ void take_row_frags(const u32x4 (&raw)[D / 16], bool valid, bf16x8 (&f)[D / 16]) {
+    asm volatile("" ::: "memory");  // the loads issued so far stay ahead of the first wait
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) f[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 v = vgpr_copy(raw[ks]);
+        f[ks] = as_bf16x8(valid ? v : u32x4{0, 0, 0, 0});
     }
 }
 
@@ -182,15 +190,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
 
     // Row constants: L2 = LSE * log2(e) (+inf for a row without a visible key or past N_q,
     // which makes its P zero), and D.
-    float l2 = INFINITY, dd = 0.f;
-    if (q_row < N_q) {
-        const float lse = LSE[(int64_t)bh * N_q + q_row];
-        l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-        dd = Dv[(int64_t)bh * N_q + q_row];
-    }
+    // All loads are issued (rows clamped to N_q - 1) before any value is taken.
+    const int q_ld = min(q_row, N_q - 1);
+    const float lse_raw = LSE[(int64_t)bh * N_q + q_ld];
+    const float dd_raw = Dv[(int64_t)bh * N_q + q_ld];
+    u32x4 q_raw[D / 16], do_raw[D / 16];
+    issue_row_loads<D>(Q + q_base + (int64_t)q_ld * D, hh, q_raw);
+    issue_row_loads<D>(dO + q_base + (int64_t)q_ld * D, hh, do_raw);
     bf16x8 qf[D / 16], dof[D / 16];
-    load_row_frags<D>(Q + q_base + (int64_t)q_row * D, q_row < N_q, hh, qf);
-    load_row_frags<D>(dO + q_base + (int64_t)q_row * D, q_row < N_q, hh, dof);
+    take_row_frags<D>(q_raw, q_row < N_q, qf);
+    take_row_frags<D>(do_raw, q_row < N_q, dof);
+    const float l2 = q_row < N_q ? (lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e) : INFINITY;
+    const float dd = q_row < N_q ? dd_raw : 0.f;
     const Offsets<D> o = operand_offsets<D>(lane);
 
     f32x16 acc[D / 32];
@@ -324,8 +335,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
 
     const Offsets<D> o = operand_offsets<D>(lane);
     bf16x8 kf[D / 16], vf[D / 16];
-    load_row_frags<D>(K + kv_base + (int64_t)key * D, key < N_k, hh, kf);
-    load_row_frags<D>(V + kv_base + (int64_t)key * D, key < N_k, hh, vf);
+    u32x4 k_raw[D / 16], v_raw[D / 16];
+    issue_row_loads<D>(K + kv_base + (int64_t)min(key, N_k - 1) * D, hh, k_raw);
+    issue_row_loads<D>(V + kv_base + (int64_t)min(key, N_k - 1) * D, hh, v_raw);
 
     f32x16 accK[D / 32], accV[D / 32];
 #pragma unroll
@@ -340,17 +352,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         stage_tile<D, SQ>(Q + base, q0, N_q, qs, w, lane);
         stage_tile<D, SQ>(dO + base, q0, N_q, os, w, lane);
     };
-    // Row constants of a tile (wave 0: lanes 0..31 L2 of rows q0 + lane, lanes 32..63 D),
-    // loaded at the start of a step and stored to LDS at its end.
+    // Row constants of a tile (waves w < SUB: lanes 0..31 L2 of rows q0 + 32*w + lane, lanes
+    // 32..63 D), loaded at the start of a step and stored to LDS at its end.  The load is
+    // unconditional (row clamped to N_q - 1, source picked per lane) and the value is fixed
+    // up only where it is stored: a per-lane choice between loads makes the wave wait for
+    // the load -- and so for the tile copies issued just before it -- before the step's work.
     auto load_ld = [&](int s) -> float {
         const int64_t rb = ((int64_t)b * H + head_of(s)) * N_q;
-        const int q = q0_of(s) + 32 * w + l32;
-        if (q >= N_q) return hh == 0 ? INFINITY : 0.f;  // rows past N_q: P = 0
-        if (hh == 0) {
-            const float lse = LSE[rb + q];
-            return lse == -INFINITY ? INFINITY : lse * kLog2e;
-        }
-        return Dv[rb + q];
+        const int q = min(q0_of(s) + 32 * w + l32, N_q - 1);
+        return (hh == 0 ? LSE : Dv)[rb + q];
+    };
+    auto fix_ld = [&](int s, float v) -> float {
+        if (q0_of(s) + 32 * w + l32 >= N_q) return hh == 0 ? INFINITY : 0.f;  // rows past N_q: P = 0
+        return hh == 0 ? (v == -INFINITY ? INFINITY : v * kLog2e) : v;
     };
     auto compute_sub = [&](int q0, const uint16_t* qs, const uint16_t* os, const float* l2p, const float* ddp) {
         if (CAUSAL && q0 + BQ - 1 + off < k0w) return;  // no row of the tile sees a key of this wave
@@ -396,10 +410,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     };
     const int ld_slot = (lane >> 5) * SQ + 32 * w + (lane & 31);  // waves 0..SUB-1 load row constants
 
+    float ld0 = 0.f;
     if (n_steps > 0) {
         stage(0, q_s0, o_s0);
-        if (w < SUB) ld_s[0][ld_slot] = load_ld(0);
+        if (w < SUB) ld0 = load_ld(0);
     }
+    take_row_frags<D>(k_raw, key < N_k, kf);
+    take_row_frags<D>(v_raw, key < N_k, vf);
+    if (n_steps > 0 && w < SUB) ld_s[0][ld_slot] = fix_ld(0, ld0);
     wait_vmem();
     __syncthreads();
     for (int s = 0; s < n_steps; s += 2) {
@@ -408,8 +426,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
             stage(s + 1, q_s1, o_s1);
             if (w < SUB) nxt = load_ld(s + 1);
         }
+        __builtin_amdgcn_sched_barrier(0);  // the fix-up of nxt stays after the step's work
         compute(s, q_s0, o_s0, ld_s[0]);
-        if (w < SUB && s + 1 < n_steps) ld_s[1][ld_slot] = nxt;
+        if (w < SUB && s + 1 < n_steps) ld_s[1][ld_slot] = fix_ld(s + 1, nxt);
         wait_vmem();
         __syncthreads();
         if (s + 1 >= n_steps) break;
@@ -417,8 +436,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
             stage(s + 2, q_s0, o_s0);
             if (w < SUB) nxt = load_ld(s + 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
         compute(s + 1, q_s1, o_s1, ld_s[1]);
-        if (w < SUB && s + 2 < n_steps) ld_s[0][ld_slot] = nxt;
+        if (w < SUB && s + 2 < n_steps) ld_s[0][ld_slot] = fix_ld(s + 2, nxt);
         wait_vmem();
         __syncthreads();
     }
@@ -494,7 +514,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
 
     const Offsets<D> o = operand_offsets<D>(lane);
     bf16x8 frag[D / 16];  // K rows (P wave) or V rows (dS wave)
-    load_row_frags<D>((ds_wave ? V : K) + kv_base + (int64_t)key * D, key < N_k, hh, frag);
+    u32x4 f_raw[D / 16];
+    issue_row_loads<D>((ds_wave ? V : K) + kv_base + (int64_t)min(key, N_k - 1) * D, hh, f_raw);
 
     f32x16 acc[D / 32];  // dV (P wave) or dK (dS wave)
 #pragma unroll
@@ -508,15 +529,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         stage_tile<D, BQ, 8>(Q + base, q0, N_q, qs, w, lane);
         stage_tile<D, BQ, 8>(dO + base, q0, N_q, os, w, lane);
     };
+    // Row constants (wave 0: lanes 0..31 L2 of rows q0 + lane, lanes 32..63 D): unconditional
+    // load, value fixed up where it is stored (as in bwd_dkdv_kernel).
     auto load_ld = [&](int s) -> float {
         const int64_t rb = ((int64_t)b * H + head_of(s)) * N_q;
-        const int q = q0_of(s) + l32;
-        if (q >= N_q) return hh == 0 ? INFINITY : 0.f;  // rows past N_q: P = 0
-        if (hh == 0) {
-            const float lse = LSE[rb + q];
-            return lse == -INFINITY ? INFINITY : lse * kLog2e;
-        }
-        return Dv[rb + q];
+        const int q = min(q0_of(s) + l32, N_q - 1);
+        return (hh == 0 ? LSE : Dv)[rb + q];
+    };
+    auto fix_ld = [&](int s, float v) -> float {
+        if (q0_of(s) + l32 >= N_q) return hh == 0 ? INFINITY : 0.f;  // rows past N_q: P = 0
+        return hh == 0 ? (v == -INFINITY ? INFINITY : v * kLog2e) : v;
     };
     float4* px = reinterpret_cast<float4*>(&p_x[pr][0][lane][0]);  // chunk j at px[64 * j]
 
@@ -577,10 +599,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         }
     };
 
+    float ld0 = 0.f;
     if (n_steps > 0) {
         stage(0, q_s0, o_s0);
-        if (w == 0) ld_s[0][lane] = load_ld(0);
+        if (w == 0) ld0 = load_ld(0);
     }
+    take_row_frags<D>(f_raw, key < N_k, frag);
+    if (n_steps > 0 && w == 0) ld_s[0][lane] = fix_ld(0, ld0);
     wait_vmem();
     __syncthreads();
     for (int s = 0; s < n_steps; s += 2) {
@@ -589,8 +614,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
             stage(s + 1, q_s1, o_s1);
             if (w == 0) nxt = load_ld(s + 1);
         }
+        __builtin_amdgcn_sched_barrier(0);  // the fix-up of nxt stays after the step's work
         step(s, q_s0, o_s0, ld_s[0]);
-        if (w == 0 && s + 1 < n_steps) ld_s[1][lane] = nxt;
+        __builtin_amdgcn_sched_barrier(0);
+        if (w == 0 && s + 1 < n_steps) ld_s[1][lane] = fix_ld(s + 1, nxt);
         wait_vmem();
         __syncthreads();
         if (s + 1 >= n_steps) break;
@@ -598,8 +625,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
             stage(s + 2, q_s0, o_s0);
             if (w == 0) nxt = load_ld(s + 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
         step(s + 1, q_s1, o_s1, ld_s[1]);
-        if (w == 0 && s + 2 < n_steps) ld_s[0][lane] = nxt;
+        __builtin_amdgcn_sched_barrier(0);
+        if (w == 0 && s + 2 < n_steps) ld_s[0][lane] = fix_ld(s + 2, nxt);
         wait_vmem();
         __syncthreads();
     }
