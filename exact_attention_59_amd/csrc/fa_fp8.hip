@@ -275,21 +275,29 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
             if (last_row_w < q0w) n_w = 0;
         }
         const float sq = q_scale[(int64_t)bh * T_r + q_tile];
-        // Q^T operand: lane holds Q8[q_row][64*ks + 32*hh + e], e < 32.
-        i32x8 qf[D / 64];
+        // Q^T operand: lane holds Q8[q_row][64*ks + 32*hh + e], e < 32.  The loads are issued
+        // here (rows past N_q read row N_q - 1, no branch) and the values taken through the
+        // opaque copy only after the first tile copies are issued too (zeros past N_q).
+        u32x4 q_raw[2 * (D / 64)];
         {
-            const uint8_t* qp = Q8 + ((int64_t)bh * N_q + q_row) * D + 32 * hh;
+            const uint8_t* qp = Q8 + ((int64_t)bh * N_q + min(q_row, N_q - 1)) * D + 32 * hh;
 #pragma unroll
             for (int ks = 0; ks < D / 64; ++ks) {
-                if (q_row < N_q) {
-                    const u32x4 a = vgpr_copy(*reinterpret_cast<const u32x4*>(qp + 64 * ks));
-                    const u32x4 b2 = vgpr_copy(*reinterpret_cast<const u32x4*>(qp + 64 * ks + 16));
-                    qf[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b2[0], (int)b2[1], (int)b2[2], (int)b2[3]};
-                } else {
-                    qf[ks] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-                }
+                q_raw[2 * ks] = *reinterpret_cast<const u32x4*>(qp + 64 * ks);
+                q_raw[2 * ks + 1] = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 16);
             }
         }
+        i32x8 qf[D / 64];
+        auto take_q = [&] {
+#pragma unroll
+            for (int ks = 0; ks < D / 64; ++ks) {
+                const u32x4 a = vgpr_copy(q_raw[2 * ks]);
+                const u32x4 b2 = vgpr_copy(q_raw[2 * ks + 1]);
+                const bool ok = q_row < N_q;
+                qf[ks] = i32x8{ok ? (int)a[0] : 0, ok ? (int)a[1] : 0, ok ? (int)a[2] : 0, ok ? (int)a[3] : 0,
+                               ok ? (int)b2[0] : 0, ok ? (int)b2[1] : 0, ok ? (int)b2[2] : 0, ok ? (int)b2[3] : 0};
+            }
+        };
         const int sk_row = swz_k8<D>(l32);  // same for rows l32 and 32 + l32
         const int sv_row = swz_v8(l32);
 
@@ -376,6 +384,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
         if (n_tiles > 0) {
             dma_k(0, k_lds0);
             dma_v(0, v_lds0);
+            take_q();
             wait_vmem();
             __syncthreads();
         }

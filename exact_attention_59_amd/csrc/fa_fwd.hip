@@ -130,16 +130,17 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
         if (last_row_w < q0w) n_w = 0;  // wave entirely past the end of Q
     }
 
-    // Q fragment (B operand of S^T = K Q^T): lane holds Q[q_row][16*ks + 8*hh + e].
-    bf16x8 qf[D / 16];
-    if (q_row < N_q) {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(Q + q_base + (int64_t)q_row * D + 8 * hh);
+    // Q fragment (B operand of S^T = K Q^T): lane holds Q[q_row][16*ks + 8*hh + e].  The
+    // loads are issued here (rows past N_q read row N_q - 1, no branch) and the values taken
+    // through the opaque copy only after the first tile copies are issued too, so that the
+    // wave waits for memory once in its prologue; rows past N_q get zeros.
+    u32x4 q_raw[D / 16];
+    {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(Q + q_base + (int64_t)min(q_row, N_q - 1) * D + 8 * hh);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(vgpr_copy(qp[2 * ks]));
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+        for (int ks = 0; ks < D / 16; ++ks) q_raw[ks] = qp[2 * ks];
     }
+    bf16x8 qf[D / 16];
 
     // ---- global -> LDS copies (no registers involved).  Copy t of this wave fills LDS
     // block (w * DMA_PER_WAVE + t), 1 KB; lane l's 16 bytes land at offset 16*l in it,
@@ -320,6 +321,11 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
         dma_tile(K, 0, k_lds0, false);
         dma_tile(V, 0, v_lds0, true);
         if (n_tiles > 1) dma_tile(K, 1, k_lds1, false);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const u32x4 v = vgpr_copy(q_raw[ks]);
+            qf[ks] = as_bf16x8(q_row < N_q ? v : u32x4{0, 0, 0, 0});
+        }
         wait_vmem();
         __syncthreads();
         // Unconditional (a wave with no rows to compute ignores the result).
