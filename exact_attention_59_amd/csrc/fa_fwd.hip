@@ -114,6 +114,12 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     const int T_c = (N_k + BC - 1) / BC;
 
   auto run_tile = [&](const int q_tile) {
+    // The lane index is produced afresh for each query tile (an opaque v_mbcnt), so that the
+    // per-lane offsets below are recomputed per tile instead of being kept, and spilled,
+    // across the first tile's loop of a causal pair.
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    const int l32 = lane & 31, hh = lane >> 5;
     const int q0w = q_tile * BR + w * 32;  // first query row of this wave
     const int q_row = q0w + l32;           // this lane's query row
 
