@@ -282,15 +282,17 @@ def test_decode_full_workloads(orc, N_k, seed):
               L_ref[:, :, 0])
 
 
-def test_combine_synthetic_partials(orc):
-    """fa_combine alone on seeded partials, including segments with lse = -inf."""
+@pytest.mark.parametrize("S,d", [(9, 128), (9, 64), (1, 128), (32, 128), (33, 128), (64, 64), (100, 128)])
+def test_combine_synthetic_partials(orc, S, d):
+    """fa_combine alone on seeded partials, including segments with lse = -inf, at both head
+    dimensions and segment counts from 1 to more than one 64-lane pass."""
     import gen
 
-    say("combine synthetic")
-    B, H, S, d = 2, 3, 9, 128
+    say("combine synthetic S=%d d=%d" % (S, d))
+    B, H = 2, 3
     o_s = gen.normal_f32(41, 0, (B, H, S, d))
     lse_s = gen.normal_f32(41, 1, (B, H, S), scale=4.0)
-    lse_s[0, 0, [1, 4]] = -np.inf
+    lse_s[0, 0, [t for t in (1, 4) if t < S]] = -np.inf
     lse_s[1, 2, :] = -np.inf   # every segment empty
     o_s[1, 2] = 0.0
     o, l = fa.combine(torch.from_numpy(o_s).cuda(), torch.from_numpy(lse_s).cuda())
@@ -300,5 +302,5 @@ def test_combine_synthetic_partials(orc):
     for b in range(B):
         for h in range(H):
             L_ref[b, h], O_ref[b, h] = orc.lse_combine(lse_s[b, h].astype(np.float64), o_s[b, h].astype(np.float64))
-    check("combine synthetic", bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
+    check("combine synthetic S=%d d=%d" % (S, d), bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
     assert np.all(bf16_dev_to_f64(o)[1, 2] == 0.0)
