@@ -91,6 +91,16 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restri
         }
     }
 
+    // Every load of the block is issued before the first is used (rows past the end read the
+    // block's last row, no branch; their values are zeroed below), so that the passes do not
+    // each wait for memory in turn.
+    u32x4 raw_all[MAXP];
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        if (p * RPP >= BLK) break;  // uniform
+        const int row = min(p * RPP + rr, rows - 1);
+        raw_all[p] = *reinterpret_cast<const u32x4*>(src + (int64_t)(r0 + row) * D + 8 * sub);
+    }
     float x[MAXP][8];
     float amax = 0.f;
 #pragma unroll
@@ -98,8 +108,7 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restri
         if (p * RPP >= BLK) break;  // uniform
         const int row = p * RPP + rr;
         const bool active = row < rows;
-        u32x4 raw = u32x4{0, 0, 0, 0};
-        if (active) raw = *reinterpret_cast<const u32x4*>(src + (int64_t)(r0 + row) * D + 8 * sub);
+        const u32x4 raw = active ? raw_all[p] : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             x[p][2 * e] = bf16_bits_to_f32(raw[e] & 0xffffu);
