@@ -126,6 +126,25 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
     // loads before the next block's are requested.
     const int v_dc = lane % CPR, v_kg = lane / CPR;
     static_assert(16 % C::V_LOADS == 0, "a lane's V rows stay in one 16-key half");
+
+    // Paged cache: the block-table entries of this wave's first 32 * kPageWin blocks are read
+    // once, into registers: the wave's block k (bi = w + NW * k) takes lanes 2k and 2k + 1 of
+    // window k / 32, the pages of its keys key0 and key0 + 16.  Blocks take them with
+    // v_readlane, so the loop reads no memory for them: a table read there would be a vector
+    // load, awaited with the in-order vector-memory counter together with the other ring
+    // slot's K/V loads.  Later blocks read the table directly.
+    constexpr int kPageWin = 4;
+    int pwin[kPageWin] = {0, 0, 0, 0};
+    if constexpr (PAGED) {
+        const int* bt = pg.block_table + (int64_t)b * pg.max_pages;
+#pragma unroll
+        for (int win = 0; win < kPageWin; ++win) {
+            const int key0 = k_beg + (w + NW * (32 * win + (lane >> 1))) * KB;
+            const int idx = ((lane & 1) ? key0 + 16 : key0) >> pg.page_log2;
+            pwin[win] = bt[min(max(idx, 0), pg.max_pages - 1)];  // entries past the wave's blocks unused
+        }
+    }
+
     auto load_block = [&](int bi, u32x4 (&kr)[C::K_LOADS], u32x4 (&vr)[C::V_LOADS]) {
         const int key0 = k_beg + bi * KB;
         const bool full = key0 + KB <= k_end;
@@ -133,9 +152,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
         const uint16_t *kh0, *kh1, *vh0, *vh1;
         if constexpr (PAGED) {
             const int P = 1 << pg.page_log2;
-            const int* bt = pg.block_table + (int64_t)b * pg.max_pages;
-            const int p0 = min(max(bt[key0 >> pg.page_log2], 0), pg.num_pages - 1);
-            const int p1 = min(max(bt[min((key0 + 16) >> pg.page_log2, pg.max_pages - 1)], 0), pg.num_pages - 1);
+            const int k = (bi - w) / NW;  // this wave's k-th block (uniform)
+            int e0, e1;
+            if (k < 32 * kPageWin) {
+                const int win = k >> 5, l0 = 2 * (k & 31);
+                const int v = win == 0 ? pwin[0] : win == 1 ? pwin[1] : win == 2 ? pwin[2] : pwin[3];
+                e0 = __builtin_amdgcn_readlane(v, l0);
+                e1 = __builtin_amdgcn_readlane(v, l0 + 1);
+            } else {
+                // (taken wave-uniform, so that both paths meet in scalar registers and the
+                // window path carries no wait for these loads)
+                const int* bt = pg.block_table + (int64_t)b * pg.max_pages;
+                e0 = __builtin_amdgcn_readfirstlane(bt[key0 >> pg.page_log2]);
+                e1 = __builtin_amdgcn_readfirstlane(bt[min((key0 + 16) >> pg.page_log2, pg.max_pages - 1)]);
+            }
+            const int p0 = min(max(e0, 0), pg.num_pages - 1);
+            const int p1 = min(max(e1, 0), pg.num_pages - 1);
             const int64_t o0 = (((int64_t)p0 * H_kv + g) * P + (key0 & (P - 1))) * D;
             const int64_t o1 = (((int64_t)p1 * H_kv + g) * P + ((key0 + 16) & (P - 1))) * D;
             kh0 = K + o0;
