@@ -17,7 +17,9 @@
     python3 <repo>/bench_counters.py sq OUT/sq        # -> profiles/sq_counters.md and .json
     # kernel durations of a plain bench run:
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- python3 <repo>/bench.py
-    python3 <repo>/bench_counters.py trace OUT/trace  # -> profiles/kernel_trace.md
+    python3 <repo>/bench_counters.py trace OUT/trace [N_k=4096=OUT/trace_4096 N_k=65536=OUT/trace_65536]
+    #   -> profiles/kernel_trace.md (decode kernels by cache length from the labelled runs of
+    #      bench.py --legs decode --decode-nk NK)
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the L2 channels) are scaled by
 what the same counters read for the bench's plain 1 GiB device copy (`--legs copy`):
@@ -151,11 +153,35 @@ def trace_summary(run_dir: str, cmd: str, tail: int = 200) -> str:
     return "\n".join(out) + "\n"
 
 
+def decode_trace_summary(labelled: list) -> str:
+    """Decode kernels of one kernel-trace run per cache length (their launches share one grid
+    across cache lengths, so a single run cannot tell them apart)."""
+    out = ["", "Decode kernels by cache length (one run per length):", "",
+           "    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace_NK -o run -- "
+           "python3 <repo>/bench.py --legs decode --decode-nk NK", "",
+           "| cache length | kernel | calls | median us | average us | min us |", "|---|---|---|---|---|---|"]
+    for label, run_dir in labelled:
+        g = defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(run_dir, "run_kernel_trace.csv"))):
+            m = re.search(r"(decode_split_kernel<\d+, (?:true|false)>|combine_kernel<\d+>)", r["Kernel_Name"])
+            if m:
+                g[m.group(1)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for k, v in sorted(g.items()):
+            v = sorted(v)
+            out.append("| %s | %s | %d | %.2f | %.2f | %.2f |" % (label, k, len(v), v[len(v) // 2], sum(v) / len(v), v[0]))
+    out += ["", "The contiguous split kernel's median is its back-to-back launches over rotated cache copies "
+            "(most of its launches); `decode_split_kernel<128, true>` is the paged cache."]
+    return "\n".join(out) + "\n"
+
+
 def main():
     args = sys.argv[1:]
-    if len(args) == 2 and args[0] == "trace":
+    if len(args) >= 2 and args[0] == "trace":
         cmd = "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- python3 <repo>/bench.py"
         text = trace_summary(args[1], cmd)
+        labelled = [a.split("=", 2)[1:] for a in args[2:]]  # N_k=4096=OUT/trace_4096
+        if labelled:
+            text += decode_trace_summary([("N_k=" + l, d) for l, d in labelled])
         with open(os.path.join(ROOT, "profiles", "kernel_trace.md"), "w") as f:
             f.write(text)
         print(text)
