@@ -1,0 +1,117 @@
+"""GPU parity on seeded random shapes: forward, flash-decoding and backward against the
+fp64 oracle, element by element.
+
+The shapes are drawn once from a fixed seed and mix ragged lengths (values next to the
+tile sizes 32, 64 and 128 are favoured), query/key length mismatches under the causal
+mask, several query heads per key/value head, both head dimensions, and segment counts
+up to one key per segment; they stay small enough for the oracle to finish in seconds.
+"""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from parity_util import bf16_dev_to_f64, check, check_grads, decode_inputs, fwd_inputs, say, scale_for, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+fa = pytest.importorskip("exact_attention_59_amd")
+
+
+def _length(rng, hi):
+    """A length in [1, hi]: half the draws land within one of a multiple of 32."""
+    if rng.random() < 0.5:
+        base = 32 * int(rng.integers(1, max(2, hi // 32)))
+        return int(min(hi, max(1, base + int(rng.integers(-1, 2)))))
+    return int(rng.integers(1, hi + 1))
+
+
+def _shapes():
+    rng = np.random.default_rng(59)
+    fwd, dec, bwd = [], [], []
+    for _ in range(16):
+        H_kv = int(rng.integers(1, 4))
+        group = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        B = int(rng.integers(1, 3)) if H_kv * group > 6 else int(rng.integers(1, 4))
+        fwd.append((B, H_kv * group, H_kv, _length(rng, 700), _length(rng, 700), int(rng.choice([64, 128])),
+                    bool(rng.integers(0, 2))))
+    for _ in range(10):
+        H_kv = int(rng.integers(1, 4))
+        group = int(rng.choice([1, 4, 7, 16, 20]))
+        N_k = _length(rng, 3000)
+        S = int(rng.integers(1, min(N_k, 100) + 1))
+        dec.append((int(rng.integers(1, 3)), H_kv * group, H_kv, N_k, int(rng.choice([64, 128])), S))
+    for _ in range(8):
+        H_kv = int(rng.integers(1, 3))
+        group = int(rng.choice([1, 2, 3]))
+        bwd.append((int(rng.integers(1, 3)), H_kv * group, H_kv, _length(rng, 400), _length(rng, 400),
+                    int(rng.choice([64, 128])), bool(rng.integers(0, 2))))
+    return fwd, dec, bwd
+
+
+FWD, DEC, BWD = _shapes()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.library()  # fail loudly if libfa.so is missing
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+@pytest.mark.parametrize("B,H,H_kv,N_q,N_k,d,causal", FWD)
+def test_sweep_fwd(orc, B, H, H_kv, N_q, N_k, d, causal):
+    name = "sweep fwd%s" % str((B, H, H_kv, N_q, N_k, d, causal))
+    say(name)
+    Q, K, V = fwd_inputs(5900 + N_q + 3 * N_k + d, B, H, H_kv, N_q, N_k, d)
+    o, lse = fa.fwd(to_dev(Q), to_dev(K), to_dev(V), causal=causal)
+    torch.cuda.synchronize()
+    O_ref, L_ref = orc.attention(Q, K, V, causal=causal)
+    check(name, bf16_dev_to_f64(o), O_ref, lse.cpu().numpy(), L_ref)
+
+
+@pytest.mark.parametrize("B,H,H_kv,N_k,d,S", DEC)
+def test_sweep_decode(orc, B, H, H_kv, N_k, d, S):
+    name = "sweep decode%s" % str((B, H, H_kv, N_k, d, S))
+    say(name)
+    Q, K, V = decode_inputs(5950 + N_k + S, B, H, H_kv, N_k, d)
+    o_part, l_part = fa.decode_split(to_dev(Q[:, :, 0, :]), to_dev(K), to_dev(V), S)
+    o, l = fa.combine(o_part, l_part)
+    torch.cuda.synchronize()
+    # every segment's partial (o_s, lse_s), then the merged output
+    L = -(-N_k // S)
+    op = o_part.cpu().numpy().astype(np.float64)
+    lp = l_part.cpu().numpy().astype(np.float64)
+    for t in range(S):
+        lo, hi = min(t * L, N_k), min((t + 1) * L, N_k)
+        O_s, L_s = orc.attention(Q, K, V, k_range=(lo, hi))
+        check("%s segment %d" % (name, t), op[:, :, t], O_s[:, :, 0], lp[:, :, t], L_s[:, :, 0])
+    O_ref, L_ref = orc.attention(Q, K, V)
+    check(name + " combined", bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
+
+
+@pytest.mark.parametrize("B,H,H_kv,N_q,N_k,d,causal", BWD)
+def test_sweep_bwd(orc, B, H, H_kv, N_q, N_k, d, causal):
+    name = "sweep bwd%s" % str((B, H, H_kv, N_q, N_k, d, causal))
+    say(name)
+    scale = scale_for(d)
+    seed = 5990 + N_q + 3 * N_k + d
+    Q, K, V = fwd_inputs(seed, B, H, H_kv, N_q, N_k, d)
+    dO = gen.normal_bf16(seed, gen.TENSOR_DO, (B, H, N_q, d))
+    q, k, v, do = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    dQ, dK, dV, _ = orc.attention_bwd(Q, K, V, dO, causal=causal, scale=scale)
+    check_grads(name, (bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)), (dQ, dK, dV))
+    if causal and N_q > N_k:  # rows that see no key get exactly zero
+        assert np.all(bf16_dev_to_f64(dq)[:, :, :N_q - N_k] == 0.0), name
