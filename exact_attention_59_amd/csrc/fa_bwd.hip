@@ -481,13 +481,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H, int H_kv, int N_q, int N_k, int T_k, int BG,
     float c, float scale) {
-    constexpr int BK = kBwdBlockKeys, BQ = kBwdBlockQueries, QT = BQ * D;
+    // A step stages SQ = 2 * BQ query rows and computes them as two BQ-row halves: one
+    // exchange barrier and one copy round per 64 rows.
+    constexpr int BK = kBwdBlockKeys, BQ = kBwdBlockQueries, SUB = 2, SQ = SUB * BQ, QT = SQ * D;
     __shared__ __attribute__((aligned(1024))) uint16_t q_s0[QT];
     __shared__ __attribute__((aligned(1024))) uint16_t q_s1[QT];
     __shared__ __attribute__((aligned(1024))) uint16_t o_s0[QT];  // dO
     __shared__ __attribute__((aligned(1024))) uint16_t o_s1[QT];
-    __shared__ __attribute__((aligned(16))) float p_x[4][4][64][4];  // [pair][chunk][lane][4]: P, fp32
-    __shared__ __attribute__((aligned(16))) float ld_s[2][2 * BQ];   // [buffer][L2 of the tile's rows, then D]
+    __shared__ __attribute__((aligned(16))) float p_x[SUB][4][4][64][4];  // [half][pair][chunk][lane][4]: P, fp32
+    __shared__ __attribute__((aligned(16))) float ld_s[2][2 * SQ];        // [buffer][L2 of the tile's rows, then D]
     asm volatile("" ::"s"(dK), "s"(dV));
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -507,8 +509,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
   auto run = [&](const int kt) {
     const int k0w = kt * BK + pr * 32, key = k0w + l32;
 
-    const int n_qt = (N_q + BQ - 1) / BQ;
-    const int qt0 = CAUSAL ? min(n_qt, max(0, kt * BK - off) / BQ) : 0;
+    const int n_qt = (N_q + SQ - 1) / SQ;
+    const int qt0 = CAUSAL ? min(n_qt, max(0, kt * BK - off) / SQ) : 0;
     const int per_head = n_qt - qt0;
     const int n_steps = group * per_head;
 
@@ -522,113 +524,126 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
     auto head_of = [&](int s) { return g * group + s / per_head; };
-    auto q0_of = [&](int s) { return (qt0 + s % per_head) * BQ; };
+    auto q0_of = [&](int s) { return (qt0 + s % per_head) * SQ; };
     auto stage = [&](int s, uint16_t* qs, uint16_t* os) {
         const int64_t base = ((int64_t)b * H + head_of(s)) * N_q * D;
         const int q0 = q0_of(s);
-        stage_tile<D, BQ, 8>(Q + base, q0, N_q, qs, w, lane);
-        stage_tile<D, BQ, 8>(dO + base, q0, N_q, os, w, lane);
+        stage_tile<D, SQ, 8>(Q + base, q0, N_q, qs, w, lane);
+        stage_tile<D, SQ, 8>(dO + base, q0, N_q, os, w, lane);
     };
-    // Row constants (wave 0: lanes 0..31 L2 of rows q0 + lane, lanes 32..63 D): unconditional
-    // load, value fixed up where it is stored (as in bwd_dkdv_kernel).
+    // Row constants (waves w < SUB: lanes 0..31 L2 of rows q0 + 32*w + lane, lanes 32..63 D):
+    // unconditional load, value fixed up where it is stored (as in bwd_dkdv_kernel).
     auto load_ld = [&](int s) -> float {
         const int64_t rb = ((int64_t)b * H + head_of(s)) * N_q;
-        const int q = min(q0_of(s) + l32, N_q - 1);
+        const int q = min(q0_of(s) + 32 * w + l32, N_q - 1);
         return (hh == 0 ? LSE : Dv)[rb + q];
     };
     auto fix_ld = [&](int s, float v) -> float {
-        if (q0_of(s) + l32 >= N_q) return hh == 0 ? INFINITY : 0.f;  // rows past N_q: P = 0
+        if (q0_of(s) + 32 * w + l32 >= N_q) return hh == 0 ? INFINITY : 0.f;  // rows past N_q: P = 0
         return hh == 0 ? (v == -INFINITY ? INFINITY : v * kLog2e) : v;
     };
-    float4* px = reinterpret_cast<float4*>(&p_x[pr][0][lane][0]);  // chunk j at px[64 * j]
+    const int ld_slot = hh * SQ + 32 * w + l32;  // waves 0..SUB-1 load row constants
+    // P exchange of half h: chunk j at px[h][64 * j]
+    float4* px[SUB];
+#pragma unroll
+    for (int h = 0; h < SUB; ++h) px[h] = reinterpret_cast<float4*>(&p_x[h][pr][0][lane][0]);
 
-    // One step: both waves of a pair take part in the barrier between the two halves.
+    // One step (two BQ-row halves): both waves of a pair take part in the exchange barrier.
     auto step = [&](int s, const uint16_t* qs, const uint16_t* os, const float* lds_ld) {
         const int q0 = q0_of(s);
-        const bool active = !(CAUSAL && q0 + BQ - 1 + off < k0w);  // some row sees a key of the pair
-        f32x16 x = f32x16{};
-        bf16x8 a_op[2];
-        if (active) {
-            const uint16_t* rows = ds_wave ? os : qs;
+        f32x16 x[SUB];
+        bf16x8 a_op[SUB][2];
+        bool act[SUB];
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                x = mfma32(*reinterpret_cast<const bf16x8*>(rows + o.row[kk]), frag[kk], x);
-            if (!ds_wave) {
-                // register r holds query q0 + 8*(r/4) + 4*hh + r%4
-                const bool edge = CAUSAL && k0w + 31 > q0 + off;
-                float p[16];
+        for (int h = 0; h < SUB; ++h) {
+            const int q0h = q0 + BQ * h;
+            act[h] = !(CAUSAL && q0h + BQ - 1 + off < k0w);  // some row of the half sees a key of the pair
+            x[h] = f32x16{};
+            if (act[h]) {
+                const uint16_t* rows = (ds_wave ? os : qs) + BQ * h * D;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                    p[r] = exp2_hw(fmaf(x[r], c, -lds_ld[qr]));
-                    if (edge && key > q0 + qr + off) p[r] = 0.f;
+                for (int kk = 0; kk < D / 16; ++kk)
+                    x[h] = mfma32(*reinterpret_cast<const bf16x8*>(rows + o.row[kk]), frag[kk], x[h]);
+                if (!ds_wave) {
+                    // register r holds query q0h + 8*(r/4) + 4*hh + r%4
+                    const bool edge = CAUSAL && k0w + 31 > q0h + off;
+                    float p[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                        p[r] = exp2_hw(fmaf(x[h][r], c, -lds_ld[BQ * h + qr]));
+                        if (edge && key > q0h + qr + off) p[r] = 0.f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        px[h][64 * j] = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        a_op[h][t] = as_bf16x8(u32x4{pack_bf16x2(p[8 * t + 0], p[8 * t + 1]), pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
+                                                     pack_bf16x2(p[8 * t + 4], p[8 * t + 5]), pack_bf16x2(p[8 * t + 6], p[8 * t + 7])});
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) px[64 * j] = make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    a_op[t] = as_bf16x8(u32x4{pack_bf16x2(p[8 * t + 0], p[8 * t + 1]), pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
-                                              pack_bf16x2(p[8 * t + 4], p[8 * t + 5]), pack_bf16x2(p[8 * t + 6], p[8 * t + 7])});
             }
         }
-        __syncthreads();  // P of this tile is in LDS
-        if (active) {
+        __syncthreads();  // P of both halves is in LDS
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) {
+            if (!act[h]) continue;
             if (ds_wave) {
                 float ds[16];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float4 pv = px[64 * j];
+                    const float4 pv = px[h][64 * j];
                     const float pj[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * j + e;
                         const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                        ds[r] = pj[e] * (x[r] - lds_ld[BQ + qr]);
+                        ds[r] = pj[e] * (x[h][r] - lds_ld[SQ + BQ * h + qr]);
                     }
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    a_op[t] = as_bf16x8(u32x4{pack_bf16x2(ds[8 * t + 0], ds[8 * t + 1]), pack_bf16x2(ds[8 * t + 2], ds[8 * t + 3]),
-                                              pack_bf16x2(ds[8 * t + 4], ds[8 * t + 5]), pack_bf16x2(ds[8 * t + 6], ds[8 * t + 7])});
+                    a_op[h][t] = as_bf16x8(u32x4{pack_bf16x2(ds[8 * t + 0], ds[8 * t + 1]), pack_bf16x2(ds[8 * t + 2], ds[8 * t + 3]),
+                                                 pack_bf16x2(ds[8 * t + 4], ds[8 * t + 5]), pack_bf16x2(ds[8 * t + 6], ds[8 * t + 7])});
             }
-            const uint16_t* cols = ds_wave ? qs : os;  // dK += dS^T Q, dV += P^T dO
+            const uint16_t* cols = (ds_wave ? qs : os) + BQ * h * D;  // dK += dS^T Q, dV += P^T dO
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a_op[t], tr_frag<D>(cols, o, db, t), acc[db]);
+                for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a_op[h][t], tr_frag<D>(cols, o, db, t), acc[db]);
         }
     };
 
     float ld0 = 0.f;
     if (n_steps > 0) {
         stage(0, q_s0, o_s0);
-        if (w == 0) ld0 = load_ld(0);
+        if (w < SUB) ld0 = load_ld(0);
     }
     take_row_frags<D>(f_raw, key < N_k, frag);
-    if (n_steps > 0 && w == 0) ld_s[0][lane] = fix_ld(0, ld0);
+    if (n_steps > 0 && w < SUB) ld_s[0][ld_slot] = fix_ld(0, ld0);
     wait_vmem();
     __syncthreads();
     for (int s = 0; s < n_steps; s += 2) {
         float nxt = 0.f;
         if (s + 1 < n_steps) {
             stage(s + 1, q_s1, o_s1);
-            if (w == 0) nxt = load_ld(s + 1);
+            if (w < SUB) nxt = load_ld(s + 1);
         }
         __builtin_amdgcn_sched_barrier(0);  // the fix-up of nxt stays after the step's work
         step(s, q_s0, o_s0, ld_s[0]);
         __builtin_amdgcn_sched_barrier(0);
-        if (w == 0 && s + 1 < n_steps) ld_s[1][lane] = fix_ld(s + 1, nxt);
+        if (w < SUB && s + 1 < n_steps) ld_s[1][ld_slot] = fix_ld(s + 1, nxt);
         wait_vmem();
         __syncthreads();
         if (s + 1 >= n_steps) break;
         if (s + 2 < n_steps) {
             stage(s + 2, q_s0, o_s0);
-            if (w == 0) nxt = load_ld(s + 2);
+            if (w < SUB) nxt = load_ld(s + 2);
         }
         __builtin_amdgcn_sched_barrier(0);
         step(s + 1, q_s1, o_s1, ld_s[1]);
         __builtin_amdgcn_sched_barrier(0);
-        if (w == 0 && s + 2 < n_steps) ld_s[0][lane] = fix_ld(s + 2, nxt);
+        if (w < SUB && s + 2 < n_steps) ld_s[0][ld_slot] = fix_ld(s + 2, nxt);
         wait_vmem();
         __syncthreads();
     }
