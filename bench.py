@@ -311,6 +311,14 @@ def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=
     b1.record(stream)
     torch.cuda.synchronize()
     b2b_ms = b0.elapsed_time(b1) / n_b2b
+    # split + combine, timed the same way
+    b0.record(stream)
+    for i in range(n_b2b):
+        fa.decode_split(q, kc[i % n_copies], vc[i % n_copies], S, o_part=o_part, lse_part=l_part)
+        fa.combine(o_part, l_part, out=o, lse=lse)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    both_b2b_ms = b0.elapsed_time(b1) / n_b2b
     del kc, vc
     # For comparison (information only): the unsplit forward with N_q = 1 on the same shapes,
     # one workgroup per (b, h), reading each K/V head once per query head of its group.
@@ -359,6 +367,7 @@ def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=
             "paged16_split_us": paged_ms * 1e3, "paged16_timing": "per repetition after a read sweep", "paged16_split_GBs": kv_bytes / (paged_ms * 1e-3) / 1e9,
             "unsplit_fwd_us": unsplit_ms * 1e3, "unsplit_fwd_GBs": kv_bytes / (unsplit_ms * 1e-3) / 1e9,
             "combine_us": sum(comb) / reps * 1e3, "end_to_end_us": sum(both) / reps * 1e3,
+            "end_to_end_b2b_us": both_b2b_ms * 1e3,
             "split_GBs": gbs, "split_pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS,
             "end_to_end_GBs": kv_bytes / (sum(both) / reps * 1e-3) / 1e9, "kv_bytes": kv_bytes}
 
