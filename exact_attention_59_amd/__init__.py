@@ -63,6 +63,9 @@ def library():
         lib.fa_decode_split_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                               f32, vp]
         lib.fa_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_decode_counter_bytes.argtypes = [i32, i32, i32]
+        lib.fa_decode_counter_bytes.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
         lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -332,13 +335,54 @@ def combine(o_part, lse_part, out=None, lse=None):
     return out, lse
 
 
-def decode(q, k, v, num_splits: int | None = None, scale: float | None = None):
-    """Split then combine on the current stream; returns (o [B,H,d] bf16, lse [B,H] fp32)."""
+def decode(q, k, v, num_splits: int | None = None, scale: float | None = None, counters=None, o_part=None,
+           lse_part=None, out=None, lse=None):
+    """fa_decode: split and merge in one launch.  q [B,H,d], k/v [B,H_kv,N_k,d] bf16 -> (o [B,H,d] bf16,
+    lse [B,H] fp32).  counters: int32 [fa_decode_counter_bytes / 4], zero before the first call and
+    left zero by every completed call (a new zeroed one is made if None); o_part / lse_part: the
+    workspace of decode_split."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
     B, H, d = q.shape
-    if num_splits is None:
-        num_splits = decode_num_splits(B, k.shape[1], k.shape[2], d)
-    o_part, lse_part = decode_split(q, k, v, num_splits, scale)
-    return combine(o_part, lse_part)
+    Bk, H_kv, N_k, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    S = int(num_splits) if num_splits is not None else decode_num_splits(B, H_kv, N_k, d)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n_counters = decode_counter_bytes(B, H, H_kv) // 4
+    if counters is None:
+        counters = torch.zeros((max(n_counters, 1),), dtype=torch.int32, device=q.device)
+    _need(counters, "counters", torch.int32, 1)
+    if counters.numel() < n_counters:
+        raise ValueError("counters must hold at least %d elements" % n_counters)
+    if o_part is None:
+        o_part = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32, 4)
+    _need(lse_part, "lse_part", torch.float32, 3)
+    if tuple(o_part.shape) != (B, H, S, d) or tuple(lse_part.shape) != (B, H, S):
+        raise ValueError("partial output shapes do not match")
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (B, H, d) or tuple(lse.shape) != (B, H):
+        raise ValueError("output shapes do not match")
+    _check("fa_decode",
+           library().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(), lse_part.data_ptr(),
+                               counters.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, N_k, d, S,
+                               float(scale), _stream_ptr(q)))
+    return out, lse
+
+
+def decode_counter_bytes(B: int, H: int, H_kv: int) -> int:
+    return int(library().fa_decode_counter_bytes(B, H, H_kv))
 
 
 def decode_num_splits(B: int, H_kv: int, N_k: int, d: int) -> int:

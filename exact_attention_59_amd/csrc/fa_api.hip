@@ -278,6 +278,36 @@ FA_EXPORT int fa_decode_num_splits(int B, int H_kv, int N_k, int d) {
     return (int)s;
 }
 
+FA_EXPORT int fa_decode(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
+                        int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
+                        int num_splits, float scale, void* stream) {
+    if (!Q || !K || !V || !O_part || !LSE_part || !counters || !O) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
+    if (H % H_kv) return FA_ERR_SHAPE;
+    if (num_splits < 1 || num_splits > N_k) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (H / H_kv > 4 * fa::kDecHeadsPerBlock) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H_kv * N_k * d >= kMaxElems || (long long)B * H * num_splits * d >= kMaxElems)
+        return FA_ERR_UNSUPPORTED;
+    const long long n_qc = (H / H_kv + fa::kDecHeadsPerBlock - 1) / fa::kDecHeadsPerBlock;
+    if ((long long)num_splits * n_qc * B * H_kv > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O_part) || misaligned(LSE_part) ||
+        misaligned(O) || (LSE && misaligned(LSE)) || (reinterpret_cast<uintptr_t>(counters) & 3u))
+        return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] decode (fused) B=%d H=%d H_kv=%d N_k=%d d=%d S=%d\n", B, H, H_kv, N_k, d, num_splits);
+    return finish(fa::launch_decode_fused(Q, K, V, O_part, LSE_part, counters, O, LSE, B, H, H_kv, N_k, d,
+                                          num_splits, scale, static_cast<hipStream_t>(stream)),
+                  "fa_decode");
+}
+
+FA_EXPORT size_t fa_decode_counter_bytes(int B, int H, int H_kv) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv) return 0;
+    const size_t n_qc = (size_t)(H / H_kv + fa::kDecHeadsPerBlock - 1) / fa::kDecHeadsPerBlock;
+    return (size_t)B * H_kv * n_qc * sizeof(int);
+}
+
 FA_EXPORT size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
     if (B <= 0 || H <= 0 || d <= 0 || num_splits <= 0) return 0;
     const size_t rows = (size_t)B * H * num_splits;

@@ -60,14 +60,31 @@ struct PagedKV {
     int page_log2, max_pages, num_pages;
 };
 
-template <int D, bool PAGED>
+// Split and combine in one launch (FUSE = true): a counter per (sequence, K/V head, head
+// chunk) counts the workgroups that have written their segment's partials; the one that
+// brings it to S merges the segments into O and LSE and sets the counter back to zero.
+struct FusedOut {
+    int* counters;  // [B][H_kv][n_qc], zero on entry
+    uint16_t* O;    // [B][H][d] bf16
+    float* LSE;     // [B][H] fp32, or null
+};
+
+// s_waitcnt operand that waits for every outstanding vector memory access (vmcnt = 0) and
+// leaves the export and LDS/scalar counters at their maxima (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, bool PAGED, bool FUSE>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __restrict__ Q,
                                                               const uint16_t* __restrict__ K,
                                                               const uint16_t* __restrict__ V,
                                                               float* __restrict__ O_part,
                                                               float* __restrict__ LSE_part, int H,
                                                               int H_kv, int N_k, int S, int L, int n_qc,
-                                                              float c, PagedKV pg) {
+                                                              float c, PagedKV pg, FusedOut fz) {
     using C = DecCfg<D>;
     constexpr int KB = C::KB, NQ = C::NQ, NW = C::NW, CPR = C::CPR;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM_BYTES];
@@ -342,10 +359,103 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
             }
             lse = (M + log2_hw(l)) * kLn2;
         }
-        float4* op = reinterpret_cast<float4*>(O_part + row * D + d0);
+        if constexpr (FUSE) {
+            // Agent-scope atomic stores write through this XCD's L2, so another XCD's
+            // workgroup can read them once they have completed (see the count below).
 #pragma unroll
-        for (int k = 0; k < DPT / 4; ++k) op[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
-        if ((tid & 15) == 0) LSE_part[row] = lse;
+            for (int k = 0; k < DPT; ++k)
+                __hip_atomic_store(O_part + row * D + d0 + k, o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((tid & 15) == 0) __hip_atomic_store(LSE_part + row, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            float4* op = reinterpret_cast<float4*>(O_part + row * D + d0);
+#pragma unroll
+            for (int k = 0; k < DPT / 4; ++k)
+                op[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+            if ((tid & 15) == 0) LSE_part[row] = lse;
+        }
+    }
+
+    if constexpr (FUSE) {
+        // Flash-decoding in one launch: the last workgroup of this (sequence, K/V head, head
+        // chunk) merges the S segments (the log-sum-exp merge of combine_kernel, taken online
+        // over chunks of segments).  Ordering without a release fence, which at agent scope
+        // writes back the XCD's whole L2 and cost ~24 us per launch here: the partials above
+        // are agent-scope atomic stores, which write through the non-coherent L2; every
+        // thread waits for its own stores to complete (vmcnt = 0) before the barrier, so when
+        // thread 0 counts, all of this workgroup's partials are in memory.  The merging
+        // workgroup reads them with agent-scope atomic loads, which do not hit a stale L2
+        // line.
+        __shared__ int is_last;
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(fz.counters + (int64_t)bg * n_qc + qc, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            is_last = old == S - 1;
+        }
+        __syncthreads();
+        if (is_last) {
+            constexpr float kLog2e = 1.4426950408889634f;
+            if (qh_out < group) {
+                const int64_t hrow = (int64_t)b * H + (g * group + qh_out);
+                const float* lp = LSE_part + hrow * S;
+                const float* op = O_part + hrow * S * D + d0;
+                // One pass over the segments, CH at a time with all of a chunk's loads in
+                // flight: running maximum M, l = sum_s e^(lse_s - M), acc = sum_s e^(lse_s - M) o_s,
+                // rescaled when M grows; lse = M + ln l and O = acc / l at the end.
+                constexpr int CH = 16;
+                float M = -INFINITY, l = 0.f, acc[DPT];
+#pragma unroll
+                for (int k = 0; k < DPT; ++k) acc[k] = 0.f;
+                for (int t0 = 0; t0 < S; t0 += CH) {
+                    float ls[CH], x[CH][DPT];
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        const int t = min(t0 + j, S - 1);  // past the end: a repeat, weighted 0 below
+                        ls[j] = ld_agent(lp + t);
+#pragma unroll
+                        for (int k = 0; k < DPT; ++k) x[j][k] = ld_agent(op + (int64_t)t * D + k);
+                    }
+                    float Mc = M;
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        if (t0 + j >= S) ls[j] = -INFINITY;
+                        Mc = fmaxf(Mc, ls[j]);
+                    }
+                    if (Mc == -INFINITY) continue;  // only empty segments so far
+                    const float r = exp2_hw((M - Mc) * kLog2e);  // 0 while M = -inf
+                    l *= r;
+#pragma unroll
+                    for (int k = 0; k < DPT; ++k) acc[k] *= r;
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        const float w = exp2_hw((ls[j] - Mc) * kLog2e);  // 0 for empty segments
+                        l += w;
+#pragma unroll
+                        for (int k = 0; k < DPT; ++k) acc[k] = fmaf(w, x[j][k], acc[k]);
+                    }
+                    M = Mc;
+                }
+                float o[DPT];
+                float lse = -INFINITY;
+                if (M != -INFINITY) {
+                    const float inv = 1.f / l;
+#pragma unroll
+                    for (int k = 0; k < DPT; ++k) o[k] = acc[k] * inv;
+                    lse = M + log2_hw(l) * kLn2;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < DPT; ++k) o[k] = 0.f;
+                }
+                uint16_t* dst = fz.O + hrow * D + d0;
+#pragma unroll
+                for (int k = 0; k < DPT / 2; ++k)
+                    *reinterpret_cast<uint32_t*>(dst + 2 * k) = pack_bf16x2(o[2 * k], o[2 * k + 1]);
+                if (fz.LSE && (tid & 15) == 0) fz.LSE[hrow] = lse;
+            }
+            if (tid == 0)  // ready for the next call
+                __hip_atomic_store(fz.counters + (int64_t)bg * n_qc + qc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -411,18 +521,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (LSE && lane == 0) LSE[row] = lse;
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool FUSE = false>
 hipError_t launch_decode_t(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
                            int B, int H, int H_kv, int N_k, int S, float scale, const PagedKV& pg,
-                           hipStream_t stream) {
+                           hipStream_t stream, const FusedOut& fz = FusedOut{nullptr, nullptr, nullptr}) {
     const int group = H / H_kv;
     const int n_qc = (group + kDecHeadsPerBlock - 1) / kDecHeadsPerBlock;
     const int L = (N_k + S - 1) / S;
     const float c = (float)((double)scale * 1.4426950408889634073599);
     const long long blocks = (long long)S * n_qc * B * H_kv;
-    hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<D, PAGED, FUSE>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-                       static_cast<const uint16_t*>(V), O_part, LSE_part, H, H_kv, N_k, S, L, n_qc, c, pg);
+                       static_cast<const uint16_t*>(V), O_part, LSE_part, H, H_kv, N_k, S, L, n_qc, c, pg, fz);
     return hipGetLastError();
 }
 
@@ -459,6 +569,18 @@ hipError_t launch_decode_split_paged(const void* Q, const void* K_pages, const v
                                          pg, stream);
     return launch_decode_t<128, true>(Q, K_pages, V_pages, O_part, LSE_part, B, H, H_kv, 0, num_splits, scale,
                                       pg, stream);
+}
+
+hipError_t launch_decode_fused(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
+                               int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
+                               int num_splits, float scale, hipStream_t stream) {
+    const PagedKV none{nullptr, nullptr, 0, 0, 0};
+    const FusedOut fz{counters, static_cast<uint16_t*>(O), LSE};
+    if (d == 64)
+        return launch_decode_t<64, false, true>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale,
+                                                none, stream, fz);
+    return launch_decode_t<128, false, true>(Q, K, V, O_part, LSE_part, B, H, H_kv, N_k, num_splits, scale, none,
+                                             stream, fz);
 }
 
 hipError_t launch_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,

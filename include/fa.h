@@ -14,6 +14,8 @@
  *                    (block table, per-sequence lengths).
  *   fa_combine       flash-decoding, step 3: exact merge of the segments by
  *                    log-sum-exp.
+ *   fa_decode        flash-decoding in one launch (split, then the merge by the
+ *                    last workgroup of each group).
  *   fa_fp8_quantize  FP8 path, step 1: random-sign Hadamard transform of Q and K
  *                    and e4m3 block quantisation of Q, K, V.
  *   fa_fwd_fp8       FP8 path, step 2: the forward on fp8 matrix cores.
@@ -210,6 +212,36 @@ int fa_decode_split_paged(const void* Q, const void* K_pages, const void* V_page
  */
 int fa_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,
                int d, int num_splits, void* stream);
+
+/*
+ * Flash-decoding in one launch (Lecture 11 section 6.2: the split step, then the
+ * exact log-sum-exp merge; section 6.4 notes that the merge kernel's fixed cost
+ * matters when segments are short): the split step of fa_decode_split, after
+ * which the last workgroup to finish for each (sequence, K/V head, group of up
+ * to 16 query heads) merges that group's segments as fa_combine does.  Results
+ * equal fa_decode_split followed by fa_combine up to the summation order of the
+ * merge.
+ *   Q, K, V, O_part, LSE_part  as for fa_decode_split (O_part, LSE_part are the
+ *                    caller's workspace, fa_decode_workspace_bytes; written)
+ *   counters         int[fa_decode_counter_bytes(B, H, H_kv) / 4], device memory,
+ *                    4-byte aligned; must be zero before the first call; every
+ *                    completed call leaves them zero again.  Calls that overlap on
+ *                    the same counters or workspace (other streams) race.
+ *   O [B][H][d] bf16 and LSE [B][H] fp32 (LSE may be NULL) as for fa_combine
+ * Validation and limits as for fa_decode_split; counters must be non-NULL.
+ * Cost: every workgroup waits for its partials to reach memory and for its count
+ * before it ends, and the merge runs after the last segment; measured back to
+ * back on MI355X (B=4, H=32, H_kv=8, d=128) this one launch took ~4 us longer
+ * than fa_decode_split + fa_combine.  It saves the caller a launch and a sync
+ * point, not GPU time.
+ */
+int fa_decode(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
+              int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
+              int num_splits, float scale, void* stream);
+
+/* Bytes of the counter array fa_decode needs: 4 * B * H_kv * ceil((H / H_kv) / 16)
+   (0 if a size is <= 0 or H is not a multiple of H_kv). */
+size_t fa_decode_counter_bytes(int B, int H, int H_kv);
 
 /*
  * Default split count for fa_decode_split (Lecture 11 section 6.4: enough

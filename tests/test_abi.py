@@ -158,6 +158,37 @@ def test_decode_validation(lib, kw, status):
     assert dec(lib, **kw) == status
 
 
+def dec_fused(lib, Q=P, K=P, V=P, Op=P, Lp=P, C=P, O=P, L=P, B=1, H=4, H_kv=1, N_k=64, d=128, S=4, scale=0.1):
+    return lib.fa_decode(Q, K, V, Op, Lp, C, O, L, B, H, H_kv, N_k, d, S, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(Op=None), fa.FA_ERR_NULL), (dict(Lp=None), fa.FA_ERR_NULL),
+    (dict(C=None), fa.FA_ERR_NULL), (dict(O=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(N_k=-5), fa.FA_ERR_SHAPE), (dict(H=5, H_kv=2), fa.FA_ERR_SHAPE),
+    (dict(S=0), fa.FA_ERR_SHAPE), (dict(S=65), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED), (dict(H=65, H_kv=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(K=P_MIS), fa.FA_ERR_ALIGN), (dict(O=P_MIS), fa.FA_ERR_ALIGN), (dict(L=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(C=ctypes.c_void_p(0x100002)), fa.FA_ERR_ALIGN),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG), (dict(scale=0.0), fa.FA_ERR_ARG),
+])
+def test_decode_fused_validation(lib, kw, status):
+    assert dec_fused(lib, **kw) == status
+
+
+def test_decode_fused_counters_need_only_4_bytes_and_lse_is_optional(lib):
+    # 4-byte aligned counters and no LSE output pass the alignment checks: the scale check, which
+    # comes after them, is what fails (nothing runs)
+    assert dec_fused(lib, C=P_MIS, L=None, scale=0.0) == fa.FA_ERR_ARG
+
+
+def test_decode_counter_bytes(lib):
+    assert fa.decode_counter_bytes(4, 32, 8) == 4 * 8 * 1 * 4
+    assert fa.decode_counter_bytes(2, 40, 2) == 2 * 2 * 2 * 4   # 20 query heads per K/V head: two chunks of 16
+    assert fa.decode_counter_bytes(0, 32, 8) == 0
+    assert fa.decode_counter_bytes(1, 6, 4) == 0
+
+
 def paged(lib, Q=P, K=P, V=P, T=P, Ls=P, Op=P, Lp=P, B=2, H=4, H_kv=1, page=16, max_pages=8, num_pages=16,
           d=128, S=4, scale=0.1):
     return lib.fa_decode_split_paged(Q, K, V, T, Ls, Op, Lp, B, H, H_kv, page, max_pages, num_pages, d, S, scale,
