@@ -44,7 +44,7 @@ COPY_BYTES = 1024 ** 3  # bench.py leg_copy: 1 GiB read and 1 GiB written per co
 
 
 def kernel_key(name: str) -> str | None:
-    m = re.search(r"(fwd_kernel<\d+, (?:true|false)>|decode_split_kernel<\d+(?:, (?:true|false))?>|combine_kernel<\d+>)",
+    m = re.search(r"(fwd_kernel<\d+, (?:true|false)>|decode_split_kernel<\d+(?:, (?:true|false)){0,2}>|combine_kernel<\d+>)",
                   name)
     if m:
         return m.group(1)
@@ -80,7 +80,7 @@ def averages(per) -> dict:
 SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
 XCDS = 8         # GRBM_GUI_ACTIVE is summed over the 8 XCDs (each has its own graphics block)
 SQ_KERNELS = r"(fwd_kernel<\d+, (?:true|false)>|fwd_fp8_kernel<\d+, (?:true|false)>|fp8_quant_kernel<\d+>|" \
-             r"bwd_\w+<\d+(?:, (?:true|false))?>|decode_split_kernel<\d+(?:, (?:true|false))?>|combine_kernel<\d+>)"
+             r"bwd_\w+<\d+(?:, (?:true|false))?>|decode_split_kernel<\d+(?:, (?:true|false)){0,2}>|combine_kernel<\d+>)"
 
 
 def sq_summary(run_dir: str, cmd: str) -> str:
@@ -163,14 +163,15 @@ def decode_trace_summary(labelled: list) -> str:
     for label, run_dir in labelled:
         g = defaultdict(list)
         for r in csv.DictReader(open(os.path.join(run_dir, "run_kernel_trace.csv"))):
-            m = re.search(r"(decode_split_kernel<\d+, (?:true|false)>|combine_kernel<\d+>)", r["Kernel_Name"])
+            m = re.search(r"(decode_split_kernel<\d+(?:, (?:true|false)){1,2}>|combine_kernel<\d+>)", r["Kernel_Name"])
             if m:
                 g[m.group(1)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         for k, v in sorted(g.items()):
             v = sorted(v)
             out.append("| %s | %s | %d | %.2f | %.2f | %.2f |" % (label, k, len(v), v[len(v) // 2], sum(v) / len(v), v[0]))
     out += ["", "The contiguous split kernel's median is its back-to-back launches over rotated cache copies "
-            "(most of its launches); `decode_split_kernel<128, true>` is the paged cache."]
+            "(most of its launches); `decode_split_kernel<128, true, false>` is the paged cache and "
+            "`decode_split_kernel<128, false, true>` the one-launch split and merge (`fa_decode`)."]
     return "\n".join(out) + "\n"
 
 

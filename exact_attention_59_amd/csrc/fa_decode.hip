@@ -326,9 +326,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
         for (int r = 0; r < 4; ++r) aa[(w * NQ + n16) * D + 16 * db + 4 * hq + r] = acc[db][r];
     __syncthreads();
 
-    // 256 threads x (D/16) outputs: thread -> query n = tid / 16, d chunk tid % 16.
+    // 256 threads x (D/16) outputs: thread -> query n = tid / 16 and columns d0 + CS*k,
+    // k < D/16.  The two-launch path takes a contiguous chunk (d0 = 16-column chunk tid % 16,
+    // CS = 1; float4 stores, which the L2 merges into whole lines).  The one-launch path
+    // writes through the L2, where each store instruction goes to memory as it is: there the
+    // 16 threads of a row interleave (d0 = tid % 16, CS = 16), so that one instruction writes
+    // 64 contiguous bytes per row instead of one dword per 32-byte sector.
     constexpr int DPT = D / 16;
-    const int n = tid >> 4, d0 = (tid & 15) * DPT;
+    constexpr int CS = FUSE ? 16 : 1;
+    const int n = tid >> 4, d0 = FUSE ? (tid & 15) : (tid & 15) * DPT;
     const int qh_out = qc * NQ + n;
     if (qh_out < group) {
         float M = -INFINITY;
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
             for (int k = 0; k < DPT; ++k) {
                 float x = 0.f;
 #pragma unroll
-                for (int v = 0; v < NW; ++v) x = fmaf(wt[v], aa[(v * NQ + n) * D + d0 + k], x);
+                for (int v = 0; v < NW; ++v) x = fmaf(wt[v], aa[(v * NQ + n) * D + d0 + CS * k], x);
                 o[k] = x * inv;
             }
             lse = (M + log2_hw(l)) * kLn2;
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
             // workgroup can read them once they have completed (see the count below).
 #pragma unroll
             for (int k = 0; k < DPT; ++k)
-                __hip_atomic_store(O_part + row * D + d0 + k, o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(O_part + row * D + d0 + CS * k, o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if ((tid & 15) == 0) __hip_atomic_store(LSE_part + row, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             float4* op = reinterpret_cast<float4*>(O_part + row * D + d0);
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
                         const int t = min(t0 + j, S - 1);  // past the end: a repeat, weighted 0 below
                         ls[j] = ld_agent(lp + t);
 #pragma unroll
-                        for (int k = 0; k < DPT; ++k) x[j][k] = ld_agent(op + (int64_t)t * D + k);
+                        for (int k = 0; k < DPT; ++k) x[j][k] = ld_agent(op + (int64_t)t * D + CS * k);
                     }
                     float Mc = M;
 #pragma unroll
@@ -449,8 +455,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
                 }
                 uint16_t* dst = fz.O + hrow * D + d0;
 #pragma unroll
-                for (int k = 0; k < DPT / 2; ++k)
-                    *reinterpret_cast<uint32_t*>(dst + 2 * k) = pack_bf16x2(o[2 * k], o[2 * k + 1]);
+                for (int k = 0; k < DPT; ++k) dst[CS * k] = (uint16_t)(pack_bf16x2(o[k], 0.f) & 0xffffu);
                 if (fz.LSE && (tid & 15) == 0) fz.LSE[hrow] = lse;
             }
             if (tid == 0)  // ready for the next call

@@ -1,5 +1,5 @@
-"""GPU parity on seeded random shapes: forward, flash-decoding and backward against the
-fp64 oracle, element by element.
+"""GPU parity on seeded random shapes: forward, flash-decoding (two launches and one) and
+backward against the fp64 oracle, element by element.
 
 The shapes are drawn once from a fixed seed and mix ragged lengths (values next to the
 tile sizes 32, 64 and 128 are favoured), query/key length mismatches under the causal
@@ -115,3 +115,23 @@ def test_sweep_bwd(orc, B, H, H_kv, N_q, N_k, d, causal):
     check_grads(name, (bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)), (dQ, dK, dV))
     if causal and N_q > N_k:  # rows that see no key get exactly zero
         assert np.all(bf16_dev_to_f64(dq)[:, :, :N_q - N_k] == 0.0), name
+
+
+@pytest.fixture(scope="module")
+def shared_counters():
+    """One counter array for every one-launch decode below, sized for the largest shape: each
+    completed call must leave it zero for the next."""
+    n = max(fa.decode_counter_bytes(B, H, H_kv) for B, H, H_kv, _, _, _ in DEC) // 4
+    return torch.zeros(n, dtype=torch.int32, device="cuda:0")
+
+
+@pytest.mark.parametrize("B,H,H_kv,N_k,d,S", DEC)
+def test_sweep_decode_one_launch(orc, shared_counters, B, H, H_kv, N_k, d, S):
+    name = "sweep one-launch decode%s" % str((B, H, H_kv, N_k, d, S))
+    say(name)
+    Q, K, V = decode_inputs(5950 + N_k + S, B, H, H_kv, N_k, d)
+    o, l = fa.decode(to_dev(Q[:, :, 0, :]), to_dev(K), to_dev(V), S, counters=shared_counters)
+    torch.cuda.synchronize()
+    O_ref, L_ref = orc.attention(Q, K, V)
+    check(name, bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
+    assert int(shared_counters.abs().sum()) == 0, name + ": a group counter was left non-zero"
