@@ -374,6 +374,23 @@ def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=
         evp[i][1].record(stream)
     torch.cuda.synchronize()
     paged_ms = sum(e[0].elapsed_time(e[1]) for e in evp) / reps
+    # the paged split + combine, and fa_decode_paged (both in one launch), timed the same way
+    for i in range(reps):
+        torch.amax(flush)
+        evp[i][0].record(stream)
+        fa.decode_split_paged(q, kp, vp, table, lens, S, o_part=o_part, lse_part=l_part)
+        fa.combine(o_part, l_part, out=o, lse=lse)
+        evp[i][1].record(stream)
+    torch.cuda.synchronize()
+    paged_both_ms = sum(e[0].elapsed_time(e[1]) for e in evp) / reps
+    fa.decode_paged(q, kp, vp, table, lens, S, counters=counters, o_part=o_part, lse_part=l_part, out=o, lse=lse)
+    for i in range(reps):
+        torch.amax(flush)
+        evp[i][0].record(stream)
+        fa.decode_paged(q, kp, vp, table, lens, S, counters=counters, o_part=o_part, lse_part=l_part, out=o, lse=lse)
+        evp[i][1].record(stream)
+    torch.cuda.synchronize()
+    paged_fused_ms = sum(e[0].elapsed_time(e[1]) for e in evp) / reps
     del kp, vp
     ms_rep = sum(split) / reps
     gbs = kv_bytes / (b2b_ms * 1e-3) / 1e9
@@ -383,6 +400,7 @@ def leg_decode(fa, torch, reps, N_k, seed, B=4, H=32, H_kv=8, d=128, num_splits=
             "split_us_per_rep": ms_rep * 1e3, "split_us_per_rep_median": split[reps // 2] * 1e3,
             "split_per_rep_GBs": kv_bytes / (ms_rep * 1e-3) / 1e9,
             "paged16_split_us": paged_ms * 1e3, "paged16_timing": "per repetition after a read sweep", "paged16_split_GBs": kv_bytes / (paged_ms * 1e-3) / 1e9,
+            "paged16_end_to_end_us": paged_both_ms * 1e3, "paged16_one_launch_us": paged_fused_ms * 1e3,
             "unsplit_fwd_us": unsplit_ms * 1e3, "unsplit_fwd_GBs": kv_bytes / (unsplit_ms * 1e-3) / 1e9,
             "combine_us": sum(comb) / reps * 1e3, "end_to_end_us": sum(both) / reps * 1e3,
             "end_to_end_b2b_us": both_b2b_ms * 1e3, "fused_b2b_us": fused_b2b_ms * 1e3,

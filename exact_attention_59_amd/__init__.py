@@ -64,6 +64,8 @@ def library():
                                               f32, vp]
         lib.fa_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, f32, vp]
         lib.fa_decode_counter_bytes.argtypes = [i32, i32, i32]
         lib.fa_decode_counter_bytes.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -378,6 +380,56 @@ def decode(q, k, v, num_splits: int | None = None, scale: float | None = None, c
            library().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(), lse_part.data_ptr(),
                                counters.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, N_k, d, S,
                                float(scale), _stream_ptr(q)))
+    return out, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits: int, scale: float | None = None,
+                 counters=None, o_part=None, lse_part=None, out=None, lse=None):
+    """fa_decode_paged: decode_split_paged and the merge in one launch -> (o [B,H,d] bf16, lse [B,H]
+    fp32).  counters as for decode (a new zeroed one is made if None)."""
+    torch = _torch()
+    for t, nm, dt, nd in ((q, "q", torch.bfloat16, 3), (k_pages, "k_pages", torch.bfloat16, 4),
+                          (v_pages, "v_pages", torch.bfloat16, 4), (block_table, "block_table", torch.int32, 2),
+                          (seq_lens, "seq_lens", torch.int32, 1)):
+        _need(t, nm, dt, nd)
+    B, H, d = q.shape
+    num_pages, H_kv, P, dk = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or dk != d:
+        raise ValueError("shape mismatch: q %s k_pages %s v_pages %s" % (tuple(q.shape), tuple(k_pages.shape),
+                                                                      tuple(v_pages.shape)))
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    max_pages = block_table.shape[1]
+    S = int(num_splits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n_counters = decode_counter_bytes(B, H, H_kv) // 4
+    if counters is None:
+        counters = torch.zeros((max(n_counters, 1),), dtype=torch.int32, device=q.device)
+    _need(counters, "counters", torch.int32, 1)
+    if counters.numel() < n_counters:
+        raise ValueError("counters must hold at least %d elements" % n_counters)
+    if o_part is None:
+        o_part = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _need(o_part, "o_part", torch.float32, 4)
+    _need(lse_part, "lse_part", torch.float32, 3)
+    if tuple(o_part.shape) != (B, H, S, d) or tuple(lse_part.shape) != (B, H, S):
+        raise ValueError("partial output shapes do not match")
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (B, H, d) or tuple(lse.shape) != (B, H):
+        raise ValueError("output shapes do not match")
+    _check("fa_decode_paged",
+           library().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                     seq_lens.data_ptr(), o_part.data_ptr(), lse_part.data_ptr(),
+                                     counters.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, P, max_pages,
+                                     num_pages, d, S, float(scale), _stream_ptr(q)))
     return out, lse
 
 

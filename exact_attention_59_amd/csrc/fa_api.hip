@@ -216,10 +216,11 @@ FA_EXPORT int fa_decode_split(const void* Q, const void* K, const void* V, float
                   "fa_decode_split");
 }
 
-FA_EXPORT int fa_decode_split_paged(const void* Q, const void* K_pages, const void* V_pages,
-                                    const int* block_table, const int* seq_lens, float* O_part,
-                                    float* LSE_part, int B, int H, int H_kv, int page_size, int max_pages,
-                                    int num_pages, int d, int num_splits, float scale, void* stream) {
+// Checks shared by the two paged entry points; sets *page_log2 on success.
+static int check_paged(const void* Q, const void* K_pages, const void* V_pages, const int* block_table,
+                       const int* seq_lens, const float* O_part, const float* LSE_part, int B, int H, int H_kv,
+                       int page_size, int max_pages, int num_pages, int d, int num_splits, float scale,
+                       int* page_log2) {
     if (!Q || !K_pages || !V_pages || !block_table || !seq_lens || !O_part || !LSE_part) return FA_ERR_NULL;
     if (B <= 0 || H <= 0 || H_kv <= 0 || page_size <= 0 || max_pages <= 0 || num_pages <= 0 || d <= 0)
         return FA_ERR_SHAPE;
@@ -228,9 +229,9 @@ FA_EXPORT int fa_decode_split_paged(const void* Q, const void* K_pages, const vo
     if (num_splits < 1 || num_splits > max_tokens) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (H / H_kv > 4 * fa::kDecHeadsPerBlock) return FA_ERR_UNSUPPORTED;
-    int page_log2 = 0;
-    while ((1 << page_log2) < page_size && page_log2 < 30) ++page_log2;
-    if ((1 << page_log2) != page_size || page_size < 16 || page_size > 4096) return FA_ERR_UNSUPPORTED;
+    int lg = 0;
+    while ((1 << lg) < page_size && lg < 30) ++lg;
+    if ((1 << lg) != page_size || page_size < 16 || page_size > 4096) return FA_ERR_UNSUPPORTED;
     if (max_tokens > 0x7fffffffLL || (long long)B * max_pages > 0x7fffffffLL ||
         (long long)num_pages * H_kv * page_size * d >= kMaxElems || (long long)B * H * num_splits * d >= kMaxElems)
         return FA_ERR_UNSUPPORTED;
@@ -240,6 +241,18 @@ FA_EXPORT int fa_decode_split_paged(const void* Q, const void* K_pages, const vo
         (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
         return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+    *page_log2 = lg;
+    return FA_OK;
+}
+
+FA_EXPORT int fa_decode_split_paged(const void* Q, const void* K_pages, const void* V_pages,
+                                    const int* block_table, const int* seq_lens, float* O_part,
+                                    float* LSE_part, int B, int H, int H_kv, int page_size, int max_pages,
+                                    int num_pages, int d, int num_splits, float scale, void* stream) {
+    int page_log2 = 0;
+    const int rc = check_paged(Q, K_pages, V_pages, block_table, seq_lens, O_part, LSE_part, B, H, H_kv, page_size,
+                               max_pages, num_pages, d, num_splits, scale, &page_log2);
+    if (rc != FA_OK) return rc;
     if (debug_enabled())
         fprintf(stderr, "[fa] decode_split_paged B=%d H=%d H_kv=%d P=%d max_pages=%d num_pages=%d d=%d S=%d\n", B, H,
                 H_kv, page_size, max_pages, num_pages, d, num_splits);
@@ -247,6 +260,26 @@ FA_EXPORT int fa_decode_split_paged(const void* Q, const void* K_pages, const vo
                                                 H_kv, page_log2, max_pages, num_pages, d, num_splits, scale,
                                                 static_cast<hipStream_t>(stream)),
                   "fa_decode_split_paged");
+}
+
+FA_EXPORT int fa_decode_paged(const void* Q, const void* K_pages, const void* V_pages, const int* block_table,
+                              const int* seq_lens, float* O_part, float* LSE_part, int* counters, void* O,
+                              float* LSE, int B, int H, int H_kv, int page_size, int max_pages, int num_pages,
+                              int d, int num_splits, float scale, void* stream) {
+    if (!counters || !O) return FA_ERR_NULL;
+    int page_log2 = 0;
+    const int rc = check_paged(Q, K_pages, V_pages, block_table, seq_lens, O_part, LSE_part, B, H, H_kv, page_size,
+                               max_pages, num_pages, d, num_splits, scale, &page_log2);
+    if (rc != FA_OK) return rc;
+    if (misaligned(O) || (LSE && misaligned(LSE)) || (reinterpret_cast<uintptr_t>(counters) & 3u))
+        return FA_ERR_ALIGN;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] decode_paged (fused) B=%d H=%d H_kv=%d P=%d max_pages=%d num_pages=%d d=%d S=%d\n", B,
+                H, H_kv, page_size, max_pages, num_pages, d, num_splits);
+    return finish(fa::launch_decode_paged_fused(Q, K_pages, V_pages, block_table, seq_lens, O_part, LSE_part,
+                                                counters, O, LSE, B, H, H_kv, page_log2, max_pages, num_pages, d,
+                                                num_splits, scale, static_cast<hipStream_t>(stream)),
+                  "fa_decode_paged");
 }
 
 FA_EXPORT int fa_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H, int d,

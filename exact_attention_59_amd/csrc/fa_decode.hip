@@ -576,6 +576,20 @@ hipError_t launch_decode_split_paged(const void* Q, const void* K_pages, const v
                                       pg, stream);
 }
 
+hipError_t launch_decode_paged_fused(const void* Q, const void* K_pages, const void* V_pages,
+                                     const int* block_table, const int* seq_lens, float* O_part,
+                                     float* LSE_part, int* counters, void* O, float* LSE, int B, int H, int H_kv,
+                                     int page_log2, int max_pages, int num_pages, int d, int num_splits,
+                                     float scale, hipStream_t stream) {
+    const PagedKV pg{block_table, seq_lens, page_log2, max_pages, num_pages};
+    const FusedOut fz{counters, static_cast<uint16_t*>(O), LSE};
+    if (d == 64)
+        return launch_decode_t<64, true, true>(Q, K_pages, V_pages, O_part, LSE_part, B, H, H_kv, 0, num_splits,
+                                               scale, pg, stream, fz);
+    return launch_decode_t<128, true, true>(Q, K_pages, V_pages, O_part, LSE_part, B, H, H_kv, 0, num_splits,
+                                            scale, pg, stream, fz);
+}
+
 hipError_t launch_decode_fused(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
                                int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
                                int num_splits, float scale, hipStream_t stream) {

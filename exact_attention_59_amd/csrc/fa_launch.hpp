@@ -54,6 +54,11 @@ hipError_t launch_decode_split_paged(const void* Q, const void* K_pages, const v
                                      int num_pages, int d, int num_splits, float scale, hipStream_t stream);
 
 // Split and combine in one launch (the split kernel's last workgroup per group merges).
+hipError_t launch_decode_paged_fused(const void* Q, const void* K_pages, const void* V_pages,
+                                     const int* block_table, const int* seq_lens, float* O_part,
+                                     float* LSE_part, int* counters, void* O, float* LSE, int B, int H, int H_kv,
+                                     int page_log2, int max_pages, int num_pages, int d, int num_splits,
+                                     float scale, hipStream_t stream);
 hipError_t launch_decode_fused(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
                                int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
                                int num_splits, float scale, hipStream_t stream);

@@ -237,6 +237,21 @@ int fa_decode(const void* Q, const void* K, const void* V, float* O_part, float*
               int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
               int num_splits, float scale, void* stream);
 
+/*
+ * fa_decode over a paged cache: the split step of fa_decode_split_paged, then
+ * the same in-launch merge as fa_decode.  Results equal fa_decode_split_paged
+ * followed by fa_combine up to the summation order of the merge.
+ *   Q, K_pages, V_pages, block_table, seq_lens, O_part, LSE_part, page_size,
+ *   max_pages, num_pages  as for fa_decode_split_paged
+ *   counters, O, LSE      as for fa_decode (fa_decode_counter_bytes(B, H, H_kv))
+ * Validation and limits as for fa_decode_split_paged; counters and O must be
+ * non-NULL and aligned as for fa_decode.
+ */
+int fa_decode_paged(const void* Q, const void* K_pages, const void* V_pages, const int* block_table,
+                    const int* seq_lens, float* O_part, float* LSE_part, int* counters, void* O,
+                    float* LSE, int B, int H, int H_kv, int page_size, int max_pages, int num_pages,
+                    int d, int num_splits, float scale, void* stream);
+
 /* Bytes of the counter array fa_decode needs: 4 * B * H_kv * ceil((H / H_kv) / 16)
    (0 if a size is <= 0 or H is not a multiple of H_kv). */
 size_t fa_decode_counter_bytes(int B, int H, int H_kv);

@@ -189,6 +189,23 @@ def test_decode_counter_bytes(lib):
     assert fa.decode_counter_bytes(1, 6, 4) == 0
 
 
+def paged_fused(lib, Q=P, K=P, V=P, T=P, Ls=P, Op=P, Lp=P, C=P, O=P, L=P, B=2, H=4, H_kv=1, page=16, max_pages=8,
+                num_pages=16, d=128, S=4, scale=0.1):
+    return lib.fa_decode_paged(Q, K, V, T, Ls, Op, Lp, C, O, L, B, H, H_kv, page, max_pages, num_pages, d, S, scale,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=None), fa.FA_ERR_NULL), (dict(O=None), fa.FA_ERR_NULL), (dict(T=None), fa.FA_ERR_NULL),
+    (dict(Lp=None), fa.FA_ERR_NULL), (dict(S=0), fa.FA_ERR_SHAPE), (dict(S=129), fa.FA_ERR_SHAPE),
+    (dict(page=24), fa.FA_ERR_UNSUPPORTED), (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(K=P_MIS), fa.FA_ERR_ALIGN), (dict(O=P_MIS), fa.FA_ERR_ALIGN), (dict(L=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(C=ctypes.c_void_p(0x100002)), fa.FA_ERR_ALIGN), (dict(scale=float("inf")), fa.FA_ERR_ARG),
+])
+def test_decode_paged_fused_validation(lib, kw, status):
+    assert paged_fused(lib, **kw) == status
+
+
 def paged(lib, Q=P, K=P, V=P, T=P, Ls=P, Op=P, Lp=P, B=2, H=4, H_kv=1, page=16, max_pages=8, num_pages=16,
           d=128, S=4, scale=0.1):
     return lib.fa_decode_split_paged(Q, K, V, T, Ls, Op, Lp, B, H, H_kv, page, max_pages, num_pages, d, S, scale,

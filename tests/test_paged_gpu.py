@@ -1,4 +1,5 @@
-"""GPU parity of flash-decoding over a paged key/value cache (fa_decode_split_paged).
+"""GPU parity of flash-decoding over a paged key/value cache (fa_decode_split_paged, and
+fa_decode_paged: the same split and the merge in one launch).
 
 The cache of each sequence is drawn contiguously by the seeded generator and then
 scattered over a shuffled pool of pages; the oracle computes plain attention on the
@@ -147,3 +148,31 @@ def test_paged_decode_workload(orc, P):
     O_ref, L_ref = reference(orc, Q, K, V, lens)
     check(name, bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
     check_segments(orc, name, Q[:2], K[:2], V[:2], lens[:2], S, o_part[:2], l_part[:2])
+
+
+@pytest.mark.parametrize("B,H,H_kv,lens,d,P,S", PAGED)
+def test_paged_one_launch(orc, shared_paged_counters, B, H, H_kv, lens, d, P, S):
+    """fa_decode_paged against the oracle, and its partials against fa_decode_split_paged's; one
+    counter array serves every case and must be left zero by each."""
+    name = "paged one-launch%s" % str((B, H, H_kv, lens, d, P, S))
+    say(name)
+    N = max(1, max(lens))
+    Q, K, V = decode_inputs(3000 + N + P + S, B, H, H_kv, N, d)
+    Kp, Vp, table = make_paged(K, V, lens, P, seed=N + S)
+    q, kp, vp = to_dev(Q[:, :, 0, :]), to_dev(Kp), to_dev(Vp)
+    t = torch.from_numpy(table).cuda()
+    ln = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    o_part = torch.empty((B, H, S, d), dtype=torch.float32, device="cuda")
+    l_part = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    o, l = fa.decode_paged(q, kp, vp, t, ln, S, counters=shared_paged_counters, o_part=o_part, lse_part=l_part)
+    torch.cuda.synchronize()
+    O_ref, L_ref = reference(orc, Q, K, V, lens)
+    check(name, bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
+    check_segments(orc, name, Q, K, V, lens, S, o_part, l_part)
+    assert int(shared_paged_counters.abs().sum()) == 0, name + ": a group counter was left non-zero"
+
+
+@pytest.fixture(scope="module")
+def shared_paged_counters():
+    n = max(fa.decode_counter_bytes(B, H, H_kv) for B, H, H_kv, _, _, _, _ in PAGED) // 4
+    return torch.zeros(n, dtype=torch.int32, device="cuda:0")
