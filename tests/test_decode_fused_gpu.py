@@ -100,3 +100,32 @@ def test_decode_fused_full_workload(orc, N_k, seed):
     ratio = float(((a - b).abs() / (2 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6)).max())
     assert ratio <= 1.0, "%s: |fused - two-launch| reaches %.3f bf16 ulp" % (name, ratio)
     assert float((l - l2).abs().max()) <= 1e-4, name
+
+
+def test_decode_fused_is_deterministic():
+    """The merging workgroup sums the S segments in index order, whichever workgroup finishes
+    last: repeated calls agree bit for bit, also on the paged cache."""
+    B, H, H_kv, N_k, d = 4, 32, 8, 4096, 128
+    say("fused decode determinism", (B, H, H_kv, N_k, d))
+    Q, K, V = decode_inputs(17, B, H, H_kv, N_k, d)
+    q, k, v = to_dev(Q[:, :, 0, :]), to_dev(K), to_dev(V)
+    S = fa.decode_num_splits(B, H_kv, N_k, d)
+    runs = [fa.decode(q, k, v, S) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(l.view(torch.int32), runs[0][1].view(torch.int32))
+    # the same cache as one page pool in order (pages of 64 tokens), every sequence full length
+    P = 64
+    npp = N_k // P
+    kp = k.view(B, H_kv, npp, P, d).permute(0, 2, 1, 3, 4).reshape(B * npp, H_kv, P, d).contiguous()
+    vp = v.view(B, H_kv, npp, P, d).permute(0, 2, 1, 3, 4).reshape(B * npp, H_kv, P, d).contiguous()
+    table = torch.arange(B * npp, dtype=torch.int32, device="cuda").view(B, npp)
+    lens = torch.full((B,), N_k, dtype=torch.int32, device="cuda")
+    pruns = [fa.decode_paged(q, kp, vp, table, lens, S) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in pruns[1:]:
+        assert torch.equal(o.view(torch.int16), pruns[0][0].view(torch.int16))
+        assert torch.equal(l.view(torch.int32), pruns[0][1].view(torch.int32))
+    # paged and contiguous: the same keys in the same segments, so the same bits
+    assert torch.equal(pruns[0][0].view(torch.int16), runs[0][0].view(torch.int16))
