@@ -3,27 +3,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs fwd,fwd_other,decode,...]
 
-One step = fa_fwd over the batched-prefill workload (B=16, H=16, N_q=N_k=1024, d=64,
-bf16), once without and once with the causal mask.  `value` is that step's nominal
-FLOPs (4*B*H*N_q*N_k*d, halved under the causal mask) over its GPU time, in TFLOPS.
-The other forward workloads (long-sequence causal B=2 H=16 N=8192 d=128, grouped-query
-ragged causal B=4 H=32/8 N=4095 d=128, and the batched-prefill shape at d=128) are
-reported under "also_measured".
+One step = fa_fwd over the long-sequence causal workload (B=2, H=16, N_q=N_k=8192,
+d=128, bf16, causal mask), the largest forward workload that the configurations name.
+`value` is that step's nominal FLOPs (4*B*H*N_q*N_k*d, halved under the causal mask)
+over its GPU time, in TFLOPS.  Before the timed steps the GPU runs the step for at least
+30 ms (its clock drops for about 10 ms after sustained load starts) and then W more steps.
+The other forward workloads (batched prefill B=16 H=16 N=1024 d=64 without and with the
+causal mask, grouped-query ragged causal B=4 H=32/8 N=4095 d=128, and the batched-prefill
+shape at d=128) are reported under "forward_workloads", each timed the same way.
 The flash-decoding leg (B=4, H=32, H_kv=8, d=128, N_k = 4096 and 65536; split kernel
 then combine kernel) runs in the same invocation and is reported under "decode" in
 GB/s of K+V read once, against the 8 TB/s HBM peak.  The split kernel's rate comes from
 back-to-back launches over rotated copies of the cache (at least 640 MB read between two
 uses of a copy, beyond the 256 MB last-level cache); per-repetition timings, with a 640 MB
 read sweep before each repetition, are reported beside it and for the combine.  The backward leg
-(fa_bwd on the same prefill shape) is reported under "backward", in TFLOP/s of its five
+(fa_bwd on the batched-prefill shape) is reported under "backward", in TFLOP/s of its five
 N_q x N_k x d products.  The FP8 leg (quantiser + e4m3 forward) is reported under "fp8",
 against the 5.03 PFLOP/s dense fp8 peak.
 
 Inputs are synthetic and seeded (counter-based SplitMix64 + Box-Muller, see gen/),
 already resident in device memory when timing starts.  GPU times come from HIP
 events recorded on the stream the kernels run on.  The fp64 oracle is timed on the
-host cores on a bounded sample of the same workload (cpu_baseline); it is a reported
-baseline, not a target.
+host cores on a bounded sample of the step's workload (whole (batch, head) slices of the
+long causal workload; cpu_baseline); it is a reported baseline, not a target.
 
 Prints one JSON line.  --gpus N with N > 1 exits with an explanation: this build
 measures one GPU's share only.
@@ -82,12 +84,29 @@ def fwd_flops(B, H, N_q, N_k, d, causal):
 
 
 # ---------------------------------------------------------------------------------- legs
-def leg_forward(fa, torch, steps, warmup, B=16, H=16, H_kv=16, N=1024, d=64, seed=2):
-    """The step: fa_fwd non-causal then causal on one input batch.
+HEADLINE = dict(name="long causal B=2 H=16 H_kv=16 N_q=N_k=8192 d=128 bf16", seed=3, B=2, H=16, H_kv=16, N=8192,
+                d=128, causal=True)
 
-    Timed region: `steps` steps between one pair of HIP events on the launch stream
-    (plus a device synchronisation on both sides).  Then, for the roofline, `steps`
-    back-to-back launches of the non-causal kernel alone between one event pair.
+
+def settle(torch, fn, ms=30.0, chunk=10):
+    """Run fn until at least `ms` of GPU time has passed on the current stream (clock settle)."""
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(torch.cuda.current_stream())
+    while True:
+        for _ in range(chunk):
+            fn()
+        w1.record(torch.cuda.current_stream())
+        w1.synchronize()
+        if w0.elapsed_time(w1) >= ms:
+            return
+
+
+def leg_forward(fa, torch, steps, warmup, name, seed, B, H, H_kv, N, d, causal):
+    """The step: one fa_fwd over the headline workload.
+
+    After a >= 30 ms clock settle and `warmup` untimed steps, `steps` steps run between
+    one pair of HIP events on the launch stream, with a device synchronisation on both
+    sides; one launch per step, so the step time is also the kernel's average launch time.
     """
     Q, K, V = fwd_inputs(seed, B, H, H_kv, N, d)
     q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
@@ -96,9 +115,9 @@ def leg_forward(fa, torch, steps, warmup, B=16, H=16, H_kv=16, N=1024, d=64, see
     stream = torch.cuda.current_stream()
 
     def step():
-        fa.fwd(q, k, v, causal=False, out=o, lse=lse)
-        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -111,26 +130,12 @@ def leg_forward(fa, torch, steps, warmup, B=16, H=16, H_kv=16, N=1024, d=64, see
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = e0.elapsed_time(e1) / steps
-
-    def per_launch(causal):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(steps):
-            fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
-
-    nc_ms, c_ms = per_launch(False), per_launch(True)
-    f_nc, f_c = fwd_flops(B, H, N, N, d, False), fwd_flops(B, H, N, N, d, True)
+    fl = fwd_flops(B, H, N, N, d, causal)
     return {
-        "step_ms": step_ms, "wall_ms_per_step": wall * 1e3 / steps,
-        "tflops": (f_nc + f_c) / (step_ms * 1e-3) / 1e12,
-        "noncausal": {"ms": nc_ms, "tflops": f_nc / (nc_ms * 1e-3) / 1e12},
-        "causal": {"ms": c_ms, "tflops": f_c / (c_ms * 1e-3) / 1e12},
-        "flops_noncausal": f_nc, "flops_causal": f_c,
+        "step_ms": step_ms, "wall_ms_per_step": wall * 1e3 / steps, "flops": fl,
+        "tflops": fl / (step_ms * 1e-3) / 1e12,
         # Q, K, V read once, O written once (bf16), LSE written once (fp32)
-        "bytes_noncausal": 2.0 * (2 * B * H * N * d + 2 * B * H_kv * N * d) + 4.0 * B * H * N,
+        "bytes": 2.0 * (2 * B * H * N * d + 2 * B * H_kv * N * d) + 4.0 * B * H * N,
     }
 
 
@@ -140,27 +145,19 @@ def leg_forward_other(fa, torch, reps, name, seed, B, H, H_kv, N, d, causal):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     # Warm up for at least 30 ms of GPU time, so the clock has settled (it dips for about
-    # 10 ms after sustained load starts) before the timed launches.
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record(torch.cuda.current_stream())
-    while True:
-        for _ in range(10):
-            fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-        w1.record(torch.cuda.current_stream())
-        w1.synchronize()
-        if w0.elapsed_time(w1) >= 30.0:
-            break
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    # 10 ms after sustained load starts) before the timed launches; then `reps` back-to-back
+    # launches between one event pair.
+    settle(torch, lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
     stream = torch.cuda.current_stream()
-    ev[0].record(stream)
-    for i in range(reps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
         fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-        ev[i + 1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    times = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
-    ms = sum(times) / reps
+    ms = e0.elapsed_time(e1) / reps
     fl = fwd_flops(B, H, N, N, d, causal)
-    return {"workload": name, "ms": ms, "ms_min": times[0], "tflops": fl / (ms * 1e-3) / 1e12,
+    return {"workload": name, "us": ms * 1e3, "tflops": fl / (ms * 1e-3) / 1e12,
             "pct_peak": 100.0 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
@@ -421,24 +418,28 @@ def leg_copy(torch, reps=5, mib=1024):
 
 
 def cpu_baseline(target_s=12.0):
-    """The fp64 oracle on the step's workload: full passes (both masks) until ~target_s."""
+    """The fp64 oracle on whole (batch, head) slices of the headline workload, one slice at a
+    time until about target_s (every slice of the causal workload carries the same work)."""
+    import numpy as np
+
     import oracle
 
-    B, H, N, d = 16, 16, 1024, 64
-    Q, K, V = fwd_inputs(2, B, H, H, N, d)
+    w = HEADLINE
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    Q, K, V = fwd_inputs(w["seed"], B, H, w["H_kv"], N, d)
     orc = oracle.Oracle()
     threads = oracle.host_threads()
-    flops_step = fwd_flops(B, H, N, N, d, False) + fwd_flops(B, H, N, N, d, True)
-    passes, elapsed = 0, 0.0
-    while passes == 0 or (elapsed < target_s and elapsed / passes * (passes + 1) <= 2.0 * target_s):
+    slice_flops = fwd_flops(1, 1, N, N, d, w["causal"])
+    n, elapsed = 0, 0.0
+    while n < B * H and (n == 0 or elapsed / n * (n + 1) <= target_s):
+        rows = np.arange(n * N, (n + 1) * N, dtype=np.int64)
         t0 = time.perf_counter()
-        orc.attention(Q, K, V, causal=False, nthreads=threads)
-        orc.attention(Q, K, V, causal=True, nthreads=threads)
+        orc.attention(Q, K, V, causal=w["causal"], rows=rows, nthreads=threads)
         elapsed += time.perf_counter() - t0
-        passes += 1
-    return {"value": flops_step * passes / elapsed / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "sample": "%d full pass(es) of the step (non-causal + causal, B=16 H=16 N=1024 d=64) in fp64, %.1f s"
-                      % (passes, elapsed),
+        n += 1
+    return {"value": slice_flops * n / elapsed / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d (batch, head) slices of the long causal workload (N=8192, d=128), every row, "
+                      "fp64, %.1f s" % (n, B * H, elapsed),
             "seconds": elapsed}
 
 
@@ -480,8 +481,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--legs", default="fwd,fwd_other,decode,bwd,fp8,cpu",
-                    help="comma list of fwd, fwd_other (the long-sequence, GQA and d=128 forward workloads), "
-                         "decode, bwd, fp8, cpu, copy")
+                    help="comma list of fwd (the headline step), fwd_other (the batched-prefill and grouped-query "
+                         "forward workloads), decode, bwd, fp8, cpu, copy")
     ap.add_argument("--all", action="store_true", help="add fwd_other to --legs")
     ap.add_argument("--decode-reps", type=int, default=30)
     ap.add_argument("--decode-nk", default="4096,65536", help="comma list of decode cache lengths")
@@ -503,39 +504,52 @@ def main():
     fa.library()
     torch.cuda.set_device(0)
     legs = set(args.legs.split(","))
+    w = HEADLINE
+    T_r = -(-w["N"] // 128)
+    head_grid = ((T_r + 1) // 2 if w["causal"] else T_r) * w["B"] * w["H"] * 256  # work-items of one launch
+    head_kernel = "fwd_kernel<%d, %s>" % (w["d"], "true" if w["causal"] else "false")
     out = {"metric": METRIC, "value": None, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "batched prefill B=16 H=16 H_kv=16 N_q=N_k=1024 d=64 bf16, step = non-causal + causal",
-                      "global_batch": 16, "seq_len": 1024, "heads": 16, "head_dim": 64, "parallelism": "single GPU"}}
+           "config": {"workload": w["name"] + (", causal" if w["causal"] else ""), "global_batch": w["B"],
+                      "seq_len": w["N"], "heads": w["H"], "kv_heads": w["H_kv"], "head_dim": w["d"],
+                      "causal": w["causal"], "parallelism": "single GPU"}}
 
     if "copy" in legs:
         log("copy leg", leg_copy(torch))
 
     if "fwd" in legs:
-        log("forward leg: %d warmup + %d timed steps" % (args.warmup, args.steps))
-        r = leg_forward(fa, torch, args.steps, args.warmup)
+        log("forward leg: >= 30 ms settle + %d warmup + %d timed steps" % (args.warmup, args.steps))
+        r = leg_forward(fa, torch, args.steps, args.warmup, w["name"], w["seed"], w["B"], w["H"], w["H_kv"],
+                        w["N"], w["d"], w["causal"])
         out["value"] = round(r["tflops"], 2)
         out["ms_per_step"] = round(r["step_ms"], 4)
         out["pct_bf16_peak"] = round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2)
-        out["detail"] = {"noncausal_tflops": round(r["noncausal"]["tflops"], 1),
-                         "noncausal_pct_peak": round(100 * r["noncausal"]["tflops"] / PEAK_BF16_TFLOPS, 2),
-                         "noncausal_us": round(r["noncausal"]["ms"] * 1e3, 2),
-                         "causal_tflops": round(r["causal"]["tflops"], 1),
-                         "causal_us": round(r["causal"]["ms"] * 1e3, 2),
-                         "wall_ms_per_step": round(r["wall_ms_per_step"], 4)}
-        achieved = r["flops_noncausal"] / (r["noncausal"]["ms"] * 1e-3) / 1e12
-        traffic, src = traffic_from_counters("fwd_kernel<64, false> grid=%d" % (8 * 16 * 16 * 256))
-        out["config"]["kernel_avg_us"] = {"noncausal": round(r["noncausal"]["ms"] * 1e3, 2),
-                                          "causal": round(r["causal"]["ms"] * 1e3, 2)}
-        out["roofline"] = {"kernel": "fwd_kernel<64, false> (non-causal, d=64)", "bound": "mfma",
-                           "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                           "traffic_source": src, "avg_launch_us": round(r["noncausal"]["ms"] * 1e3, 2),
-                           "algorithmic_flops_per_launch": r["flops_noncausal"],
-                           "algorithmic_bytes_per_launch": r["bytes_noncausal"],
-                           "counters": shader_counters("fwd_kernel<64, false> grid=%d" % (8 * 16 * 16 * 256))}
-        log("forward", out["detail"])
+        out["config"]["kernel_avg_us"] = round(r["step_ms"] * 1e3, 2)
+        out["config"]["wall_ms_per_step"] = round(r["wall_ms_per_step"], 4)
+        traffic, src = traffic_from_counters("%s grid=%d" % (head_kernel, head_grid))
+        out["roofline"] = {"kernel": "%s (%s)" % (head_kernel, w["name"]), "bound": "mfma",
+                           "achieved": round(r["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                           "traffic_source": src, "avg_launch_us": round(r["step_ms"] * 1e3, 2),
+                           "algorithmic_flops_per_launch": r["flops"],
+                           "algorithmic_bytes_per_launch": r["bytes"],
+                           "traffic_over_algorithmic": (round(traffic / r["bytes"], 3) if traffic else None),
+                           "counters": shader_counters("%s grid=%d" % (head_kernel, head_grid))}
+        log("forward", out["roofline"])
+
+    if "fwd_other" in legs or args.all:
+        others = [("batched prefill B=16 H=16 N=1024 d=64 non-causal", 2, 16, 16, 16, 1024, 64, False),
+                  ("batched prefill B=16 H=16 N=1024 d=64 causal", 2, 16, 16, 16, 1024, 64, True),
+                  ("GQA ragged causal B=4 H=32 H_kv=8 N=4095 d=128", 4, 4, 32, 8, 4095, 128, True),
+                  ("batched prefill B=16 H=16 N=1024 d=128 non-causal", 2, 16, 16, 16, 1024, 128, False)]
+        out["forward_workloads"] = []
+        for name, seed, B, H, H_kv, N, d, causal in others:
+            log("forward", name)
+            out["forward_workloads"].append({k: (round(v, 2) if isinstance(v, float) else v) for k, v in
+                                             leg_forward_other(fa, torch, 50, name, seed, B, H, H_kv, N, d,
+                                                               causal).items()})
+            torch.cuda.empty_cache()
 
     if "decode" in legs:
         dec = {}
@@ -560,17 +574,6 @@ def main():
         out["fp8"] = leg_fp8(fa, torch, 30)
         log("fp8", out["fp8"])
         torch.cuda.empty_cache()
-
-    if args.all or "fwd_other" in legs:
-        others = [("long causal B=2 H=16 N=8192 d=128", 3, 2, 16, 16, 8192, 128, True),
-                  ("GQA ragged causal B=4 H=32 H_kv=8 N=4095 d=128", 4, 4, 32, 8, 4095, 128, True),
-                  ("batched prefill B=16 H=16 N=1024 d=128 non-causal", 2, 16, 16, 16, 1024, 128, False)]
-        out["also_measured"] = []
-        for name, seed, B, H, H_kv, N, d, causal in others:
-            log("forward", name)
-            out["also_measured"].append({k: (round(v, 2) if isinstance(v, float) else v) for k, v in
-                                         leg_forward_other(fa, torch, 20, name, seed, B, H, H_kv, N, d,
-                                                           causal).items()})
 
     if "cpu" in legs:
         log("cpu baseline (oracle, ~%.0f s)" % args.cpu_seconds)

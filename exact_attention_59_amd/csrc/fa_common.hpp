@@ -100,6 +100,19 @@ __device__ __forceinline__ float half_swap_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The same across lanes l and l ^ 16 (v_permlane16_swap: the odd 16-lane rows of one copy
+// trade places with the even rows of the other), then across the two 32-lane halves: a
+// reduction over the 4 lanes l % 16 + 16 k, with no LDS round trip.  Every lane of a group
+// adds the same operands in the same order.
+__device__ __forceinline__ float quad_row_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return half_swap_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_row_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return half_swap_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
 // Round two floats to bf16 (RNE, v_cvt_pk_bf16_f32) and pack them, lo first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2 r;

@@ -36,7 +36,8 @@ struct DecCfg {
     static constexpr int K_LOADS = 2 * KSTEPS;    // 16-byte K loads per lane per block
     static constexpr int V_LOADS = KB * CPR / 64; // 16-byte V loads per lane per block
     static constexpr int V_ELEMS = KB * D;        // one wave's LDS V block
-    static constexpr int MERGE_FLOATS = NW * NQ * (D + 2);
+    static constexpr int NQP = NQ + 4;            // padded query stride of the merge buffer
+    static constexpr int MERGE_FLOATS = 2 * NW * NQ + NW * D * NQP;
     static constexpr int SMEM_BYTES =
         (NW * V_ELEMS * 2 > MERGE_FLOATS * 4) ? NW * V_ELEMS * 2 : MERGE_FLOATS * 4;
     static_assert(V_LOADS * 64 == KB * CPR, "V block must split evenly over the lanes");
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[mb][r]);
-        mx = xor_max(xor_max(mx, 16), 32);
+        mx = quad_row_max(mx);
         const float t_max = mx * c;
         if (t_max > m2) {  // per lane: the decode state is tiny, rescale whenever the max grows
             const float alpha = exp2_hw(m2 - t_max);  // 0 when m2 = -inf
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
                 sc[mb][r] = p;
                 ps += p;
             }
-        lsum += xor_sum(xor_sum(ps, 16), 32);
+        lsum += quad_row_sum(ps);
         // P^T as B operand: slot e <-> key 16*(e/4) + 4*hq + e%4.
         const bf16x8 pf = as_bf16x8(u32x4{pack_bf16x2(sc[0][0], sc[0][1]), pack_bf16x2(sc[0][2], sc[0][3]),
                                           pack_bf16x2(sc[1][0], sc[1][1]), pack_bf16x2(sc[1][2], sc[1][3])});
@@ -311,11 +312,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
             compute(bi + NW, k_end, k1, v1, [&] { if (bi + 3 * NW < nblk) load_block(bi + 3 * NW, k1, v1); });
     }
 
-    // Merge the 4 wave states through LDS (reusing the V blocks).
+    // Merge the 4 wave states through LDS (reusing the V blocks).  The accumulators are laid
+    // out d-major with a padded query stride, [NW][D][NQ + 4]: one store instruction (lanes
+    // n16 = 0..15, hq = 0..3 at d = 16 db + 4 hq + r) and one load instruction below (16
+    // columns d0 x 4 queries) each touch 64 distinct banks.
     __syncthreads();
     float* mm = reinterpret_cast<float*>(smem);  // [NW][NQ]
     float* ll = mm + NW * NQ;                    // [NW][NQ]
-    float* aa = ll + NW * NQ;                    // [NW][NQ][D]
+    float* aa = ll + NW * NQ;                    // [NW][D][NQP]
+    constexpr int NQP = C::NQP;
     if (hq == 0) {
         mm[w * NQ + n16] = m2;
         ll[w * NQ + n16] = lsum;
@@ -323,18 +328,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) aa[(w * NQ + n16) * D + 16 * db + 4 * hq + r] = acc[db][r];
+        for (int r = 0; r < 4; ++r) aa[(w * D + 16 * db + 4 * hq + r) * NQP + n16] = acc[db][r];
     __syncthreads();
 
-    // 256 threads x (D/16) outputs: thread -> query n = tid / 16 and columns d0 + CS*k,
-    // k < D/16.  The two-launch path takes a contiguous chunk (d0 = 16-column chunk tid % 16,
-    // CS = 1; float4 stores, which the L2 merges into whole lines).  The one-launch path
-    // writes through the L2, where each store instruction goes to memory as it is: there the
-    // 16 threads of a row interleave (d0 = tid % 16, CS = 16), so that one instruction writes
-    // 64 contiguous bytes per row instead of one dword per 32-byte sector.
+    // 256 threads x (D/16) outputs: thread -> query n = tid / 16 and columns d0 + 16 k
+    // (d0 = tid % 16, k < D/16): the 16 threads of a row interleave, so that one store
+    // instruction writes 64 contiguous bytes per row (the one-launch path writes through
+    // the L2, where each store instruction goes to memory as it is).
     constexpr int DPT = D / 16;
-    constexpr int CS = FUSE ? 16 : 1;
-    const int n = tid >> 4, d0 = FUSE ? (tid & 15) : (tid & 15) * DPT;
+    constexpr int CS = 16;
+    const int n = tid >> 4, d0 = tid & 15;
     const int qh_out = qc * NQ + n;
     if (qh_out < group) {
         float M = -INFINITY;
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
             for (int k = 0; k < DPT; ++k) {
                 float x = 0.f;
 #pragma unroll
-                for (int v = 0; v < NW; ++v) x = fmaf(wt[v], aa[(v * NQ + n) * D + d0 + CS * k], x);
+                for (int v = 0; v < NW; ++v) x = fmaf(wt[v], aa[(v * D + d0 + CS * k) * NQP + n], x);
                 o[k] = x * inv;
             }
             lse = (M + log2_hw(l)) * kLn2;
@@ -373,10 +376,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
                 __hip_atomic_store(O_part + row * D + d0 + CS * k, o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if ((tid & 15) == 0) __hip_atomic_store(LSE_part + row, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
-            float4* op = reinterpret_cast<float4*>(O_part + row * D + d0);
 #pragma unroll
-            for (int k = 0; k < DPT / 4; ++k)
-                op[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+            for (int k = 0; k < DPT; ++k) O_part[row * D + d0 + CS * k] = o[k];
             if ((tid & 15) == 0) LSE_part[row] = lse;
         }
     }
