@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_PKG, "libfa.so")
 _lib = None
 
-FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = range(7)
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP, FA_ERR_CAPACITY = range(8)
 
 
 class FAError(RuntimeError):
@@ -66,6 +66,7 @@ def library():
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
         lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                         i32, f32, vp]
+        lib.fa_decode_static.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
         lib.fa_decode_counter_bytes.argtypes = [i32, i32, i32]
         lib.fa_decode_counter_bytes.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -76,7 +77,7 @@ def library():
         lib.fa_fwd_tile_count.restype = ctypes.c_longlong
         lib.fa_strerror.argtypes = [i32]
         lib.fa_strerror.restype = ctypes.c_char_p
-        for fn in (lib.fa_fwd, lib.fa_bwd, lib.fa_fp8_quantize, lib.fa_fwd_fp8, lib.fa_fp8_block_rows, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits,
+        for fn in (lib.fa_fwd, lib.fa_bwd, lib.fa_fp8_quantize, lib.fa_fwd_fp8, lib.fa_fp8_block_rows, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits, lib.fa_decode_static,
                    lib.fa_fwd_tile_shape):
             fn.restype = i32
         _lib = lib
@@ -382,6 +383,35 @@ def decode(q, k, v, num_splits: int | None = None, scale: float | None = None, c
                                float(scale), _stream_ptr(q)))
     return out, lse
 
+
+
+def decode_static(q, k, v, num_splits: int | None = None, scale: float | None = None, out=None, lse=None):
+    """fa_decode_static: fa_decode with its partials and counters in the library's static device
+    scratch array (no workspace from the caller, no allocation in the call).  q [B,H,d], k/v
+    [B,H_kv,N_k,d] bf16 -> (o [B,H,d] bf16, lse [B,H] fp32).  Calls that overlap on one device race."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, H, d = q.shape
+    Bk, H_kv, N_k, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    S = int(num_splits) if num_splits is not None else decode_num_splits(B, H_kv, N_k, d)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (B, H, d) or tuple(lse.shape) != (B, H):
+        raise ValueError("output shapes do not match")
+    _check("fa_decode_static",
+           library().fa_decode_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      B, H, H_kv, N_k, d, S, float(scale), _stream_ptr(q)))
+    return out, lse
 
 def decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits: int, scale: float | None = None,
                  counters=None, o_part=None, lse_part=None, out=None, lse=None):

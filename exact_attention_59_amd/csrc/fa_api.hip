@@ -61,6 +61,7 @@ FA_EXPORT const char* fa_strerror(int status) {
         case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case FA_ERR_ARG: return "invalid argument (scale not finite and positive, or a flag not 0/1)";
         case FA_ERR_HIP: return "the HIP runtime reported an error while enqueueing";
+        case FA_ERR_CAPACITY: return "the problem needs more than fa_decode_static's static scratch array holds (16 MiB: counters, LSE_part and O_part)";
         default: return "unknown status";
     }
 }
@@ -333,6 +334,32 @@ FA_EXPORT int fa_decode(const void* Q, const void* K, const void* V, float* O_pa
     return finish(fa::launch_decode_fused(Q, K, V, O_part, LSE_part, counters, O, LSE, B, H, H_kv, N_k, d,
                                           num_splits, scale, static_cast<hipStream_t>(stream)),
                   "fa_decode");
+}
+
+FA_EXPORT int fa_decode_static(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                               int H_kv, int N_k, int d, int num_splits, float scale, void* stream) {
+    if (!Q || !K || !V || !O) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
+    if (H % H_kv) return FA_ERR_SHAPE;
+    if (num_splits < 1 || num_splits > N_k) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (H / H_kv > 4 * fa::kDecHeadsPerBlock) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H_kv * N_k * d >= kMaxElems) return FA_ERR_UNSUPPORTED;
+    const long long n_qc = (H / H_kv + fa::kDecHeadsPerBlock - 1) / fa::kDecHeadsPerBlock;
+    if ((long long)num_splits * n_qc * B * H_kv > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    // capacity of the static scratch array: the counters and both partial arrays
+    if ((long long)B * H_kv * n_qc * (long long)sizeof(int) > (long long)fa::kStaticCounterBytes ||
+        (long long)B * H * num_splits * (d + 1) > (long long)(fa::kStaticScratchBytes / sizeof(float)) ||
+        fa::decode_static_bytes(B, H, d, num_splits) > fa::kStaticScratchBytes)
+        return FA_ERR_CAPACITY;
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || (LSE && misaligned(LSE))) return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] decode (static scratch) B=%d H=%d H_kv=%d N_k=%d d=%d S=%d\n", B, H, H_kv, N_k, d,
+                num_splits);
+    return finish(fa::launch_decode_static(Q, K, V, O, LSE, B, H, H_kv, N_k, d, num_splits, scale,
+                                           static_cast<hipStream_t>(stream)),
+                  "fa_decode_static");
 }
 
 FA_EXPORT size_t fa_decode_counter_bytes(int B, int H, int H_kv) {

@@ -20,10 +20,21 @@
 //     registers, each load instruction reading whole 64-byte lines of 16 key rows;
 //   - O^T += V^T P^T: V is written row-major (XOR-swizzled chunks) to the wave's own
 //     LDS block and read back with the transposing LDS read in the key order of P^T.
+#include <mutex>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
+
+// ---- fa_decode_static: the one-launch decode with its partials and group counters in a
+// file-scope device array instead of caller workspaces (for callers that cannot allocate).
+// Layout: [counters: kStaticCounterBytes][LSE_part][O_part], each region 256-byte aligned.
+// Each device holds its own copy for the life of the process; every call on a device uses
+// that device's copy, so calls that overlap on one device race.  Host code uses the
+// device address from hipGetSymbolAddress (static_scratch below), never this name.
+__device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
 
 template <int D>
@@ -551,7 +562,62 @@ hipError_t launch_combine_t(const float* O_part, const float* LSE_part, void* O,
     return hipGetLastError();
 }
 
+__global__ void zero_ints_kernel(int* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's scratch array, looked up once per device (with that
+// device current).  `fresh` is set on the first call on a device: its counters must be
+// cleared before first use.
+hipError_t static_scratch(unsigned char** out, bool* fresh) {
+    static std::mutex mu;
+    static unsigned char* ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    *fresh = false;
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptr[dev] = static_cast<unsigned char*>(p);
+        *fresh = true;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
+
+size_t decode_static_bytes(int B, int H, int d, int num_splits) {
+    const size_t rows = (size_t)B * H * num_splits;
+    const size_t lse = (rows * sizeof(float) + 255) / 256 * 256;
+    return kStaticCounterBytes + lse + rows * (size_t)d * sizeof(float);
+}
+
+hipError_t launch_decode_static(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                int H_kv, int N_k, int d, int num_splits, float scale, hipStream_t stream) {
+    unsigned char* base = nullptr;
+    bool fresh = false;
+    hipError_t e = static_scratch(&base, &fresh);
+    if (e != hipSuccess) return e;
+    int* counters = reinterpret_cast<int*>(base);
+    if (fresh) {  // the group counters start at zero; every completed call leaves them zero
+        hipLaunchKernelGGL(zero_ints_kernel, dim3(16), dim3(256), 0, stream, counters,
+                           (int)(kStaticCounterBytes / sizeof(int)));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const size_t rows = (size_t)B * H * num_splits;
+    float* lse_part = reinterpret_cast<float*>(base + kStaticCounterBytes);
+    float* o_part = reinterpret_cast<float*>(base + kStaticCounterBytes + (rows * sizeof(float) + 255) / 256 * 256);
+    return launch_decode_fused(Q, K, V, o_part, lse_part, counters, O, LSE, B, H, H_kv, N_k, d, num_splits, scale,
+                               stream);
+}
 
 hipError_t launch_decode_split(const void* Q, const void* K, const void* V, float* O_part,
                                float* LSE_part, int B, int H, int H_kv, int N_k, int d, int num_splits,

@@ -63,6 +63,14 @@ hipError_t launch_decode_fused(const void* Q, const void* K, const void* V, floa
                                int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
                                int num_splits, float scale, hipStream_t stream);
 
+// fa_decode_static: fa_decode with its workspace and counters in a file-scope device array
+// of kStaticScratchBytes (no allocation); the first call on a device clears its counters.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr size_t kStaticCounterBytes = (size_t)64 << 10;
+size_t decode_static_bytes(int B, int H, int d, int num_splits);  // counters + LSE_part + O_part
+hipError_t launch_decode_static(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                int H_kv, int N_k, int d, int num_splits, float scale, hipStream_t stream);
+
 hipError_t launch_combine(const float* O_part, const float* LSE_part, void* O, float* LSE, int B, int H,
                           int d, int num_splits, hipStream_t stream);
 

@@ -61,7 +61,8 @@ typedef enum {
     FA_ERR_UNSUPPORTED = 3, /* head dimension d not in {64, 128}, or a size beyond the limits below */
     FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
     FA_ERR_ARG = 5,         /* scale not finite and positive, or a 0/1 flag out of range */
-    FA_ERR_HIP = 6          /* the HIP runtime reported an error when enqueueing */
+    FA_ERR_HIP = 6,         /* the HIP runtime reported an error when enqueueing */
+    FA_ERR_CAPACITY = 7     /* fa_decode_static: the problem does not fit its static scratch array */
 } fa_status;
 
 /*
@@ -251,6 +252,27 @@ int fa_decode_paged(const void* Q, const void* K_pages, const void* V_pages, con
                     const int* seq_lens, float* O_part, float* LSE_part, int* counters, void* O,
                     float* LSE, int B, int H, int H_kv, int page_size, int max_pages, int num_pages,
                     int d, int num_splits, float scale, void* stream);
+
+/*
+ * fa_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernel
+ * and results as fa_decode with the same num_splits, but O_part, LSE_part and the
+ * group counters live in a file-scope device array of the library, 16 MiB per
+ * device, held from the first call on a device until the process ends.  The
+ * entry point calls no hipMalloc, hipFree or other allocating routine.
+ *   Q [B][H][d], K, V [B][H_kv][N_k][d] bf16, read
+ *   O [B][H][d] bf16 and LSE [B][H] fp32 (LSE may be NULL), written
+ * Capacity: 4 * B * H_kv * ceil((H / H_kv) / 16) <= 64 KiB of counters, and
+ * 4 * B * H * num_splits * (d + 1) bytes of partials (each part rounded up to 256
+ * bytes) within the remaining 16 MiB - 64 KiB; otherwise FA_ERR_CAPACITY and no
+ * work is enqueued.  Other validation as for fa_decode.
+ * The first call on a device looks up that device's copy of the array and clears
+ * its counters on `stream` (one small extra kernel); every completed call leaves
+ * them zero.  All calls on one device share its array: calls that overlap on a
+ * device (other streams, other threads) race.
+ */
+int fa_decode_static(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                     int H_kv, int N_k, int d, int num_splits, float scale, void* stream);
 
 /* Bytes of the counter array fa_decode needs: 4 * B * H_kv * ceil((H / H_kv) / 16)
    (0 if a size is <= 0 or H is not a multiple of H_kv). */

@@ -182,6 +182,36 @@ def test_decode_fused_counters_need_only_4_bytes_and_lse_is_optional(lib):
     assert dec_fused(lib, C=P_MIS, L=None, scale=0.0) == fa.FA_ERR_ARG
 
 
+def dec_static(lib, Q=P, K=P, V=P, O=P, L=P, B=1, H=4, H_kv=1, N_k=64, d=128, S=4, scale=0.1):
+    return lib.fa_decode_static(Q, K, V, O, L, B, H, H_kv, N_k, d, S, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(O=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=5, H_kv=2), fa.FA_ERR_SHAPE), (dict(S=65), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED), (dict(H=65, H_kv=1), fa.FA_ERR_UNSUPPORTED),
+    # beyond the 16 MiB static array: 4*32*1000*(128+1)*4 bytes of partials
+    (dict(B=4, H=32, H_kv=8, N_k=4096, S=1000), fa.FA_ERR_CAPACITY),
+    # more group counters than its 64 KiB hold
+    (dict(B=20000, H=8, H_kv=1, N_k=64, S=1), fa.FA_ERR_CAPACITY),
+    (dict(K=P_MIS), fa.FA_ERR_ALIGN), (dict(L=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(scale=float("nan")), fa.FA_ERR_ARG), (dict(scale=0.0), fa.FA_ERR_ARG),
+])
+def test_decode_static_validation(lib, kw, status):
+    assert dec_static(lib, **kw) == status
+
+
+def test_decode_static_capacity_boundary(lib):
+    # the flash-decoding workload fits at 16 and 64 segments (checks pass up to the scale check) ...
+    assert dec_static(lib, B=4, H=32, H_kv=8, N_k=65536, S=16, scale=0.0) == fa.FA_ERR_ARG
+    assert dec_static(lib, B=4, H=32, H_kv=8, N_k=65536, S=64, scale=0.0) == fa.FA_ERR_ARG
+    # ... and 4*32*S*129*4 bytes (+ 64 KiB of counters) first exceeds 16 MiB at S = 254
+    assert dec_static(lib, B=4, H=32, H_kv=8, N_k=65536, S=253, scale=0.0) == fa.FA_ERR_ARG
+    assert dec_static(lib, B=4, H=32, H_kv=8, N_k=65536, S=254, scale=0.0) == fa.FA_ERR_CAPACITY
+    # LSE is optional
+    assert dec_static(lib, L=None, scale=0.0) == fa.FA_ERR_ARG
+
+
 def test_decode_counter_bytes(lib):
     assert fa.decode_counter_bytes(4, 32, 8) == 4 * 8 * 1 * 4
     assert fa.decode_counter_bytes(2, 40, 2) == 2 * 2 * 2 * 4   # 20 query heads per K/V head: two chunks of 16
@@ -247,8 +277,8 @@ def test_combine_validation(lib, kw, status):
 
 
 def test_strerror_covers_every_status(lib):
-    texts = {fa.strerror(s) for s in range(7)}
-    assert len(texts) == 7
+    texts = {fa.strerror(s) for s in range(8)}
+    assert len(texts) == 8
     assert fa.strerror(99) == "unknown status"
 
 
