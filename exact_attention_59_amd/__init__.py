@@ -67,6 +67,8 @@ def library():
         lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                         i32, f32, vp]
         lib.fa_decode_static.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_decode_counters_reset.argtypes = [vp, i32, i32, i32, vp]
+        lib.fa_decode_counters_check.argtypes = [vp, i32, i32, i32, vp, vp]
         lib.fa_decode_counter_bytes.argtypes = [i32, i32, i32]
         lib.fa_decode_counter_bytes.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -78,6 +80,7 @@ def library():
         lib.fa_strerror.argtypes = [i32]
         lib.fa_strerror.restype = ctypes.c_char_p
         for fn in (lib.fa_fwd, lib.fa_bwd, lib.fa_fp8_quantize, lib.fa_fwd_fp8, lib.fa_fp8_block_rows, lib.fa_decode_split, lib.fa_decode_split_paged, lib.fa_combine, lib.fa_decode_num_splits, lib.fa_decode_static,
+                   lib.fa_decode_counters_reset, lib.fa_decode_counters_check,
                    lib.fa_fwd_tile_shape):
             fn.restype = i32
         _lib = lib
@@ -339,11 +342,12 @@ def combine(o_part, lse_part, out=None, lse=None):
 
 
 def decode(q, k, v, num_splits: int | None = None, scale: float | None = None, counters=None, o_part=None,
-           lse_part=None, out=None, lse=None):
+           lse_part=None, out=None, lse=None, check_counters: bool = False):
     """fa_decode: split and merge in one launch.  q [B,H,d], k/v [B,H_kv,N_k,d] bf16 -> (o [B,H,d] bf16,
     lse [B,H] fp32).  counters: int32 [fa_decode_counter_bytes / 4], zero before the first call and
     left zero by every completed call (a new zeroed one is made if None); o_part / lse_part: the
-    workspace of decode_split."""
+    workspace of decode_split.  check_counters: verify (with fa_decode_counters_check and a
+    synchronisation) that caller-provided counters are zero, and raise instead of launching if not."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 4)
@@ -361,6 +365,11 @@ def decode(q, k, v, num_splits: int | None = None, scale: float | None = None, c
     _need(counters, "counters", torch.int32, 1)
     if counters.numel() < n_counters:
         raise ValueError("counters must hold at least %d elements" % n_counters)
+    if check_counters:
+        bad = decode_counters_check(counters, B, H, H_kv)
+        if bad:
+            raise RuntimeError("fa_decode: %d group counter(s) are not zero (never cleared, or shared by overlapping "
+                               "calls); clear them with decode_counters_reset" % bad)
     if o_part is None:
         o_part = torch.empty((B, H, S, d), dtype=torch.float32, device=q.device)
     if lse_part is None:
@@ -383,6 +392,28 @@ def decode(q, k, v, num_splits: int | None = None, scale: float | None = None, c
                                float(scale), _stream_ptr(q)))
     return out, lse
 
+
+
+def decode_counters_reset(counters, B: int, H: int, H_kv: int):
+    """fa_decode_counters_reset: zero the group counters of fa_decode on the current stream."""
+    torch = _torch()
+    _need(counters, "counters", torch.int32, 1)
+    if counters.numel() < decode_counter_bytes(B, H, H_kv) // 4:
+        raise ValueError("counters too small")
+    _check("fa_decode_counters_reset",
+           library().fa_decode_counters_reset(counters.data_ptr(), B, H, H_kv, _stream_ptr(counters)))
+
+
+def decode_counters_check(counters, B: int, H: int, H_kv: int) -> int:
+    """fa_decode_counters_check: the number of non-zero group counters (synchronises the stream)."""
+    torch = _torch()
+    _need(counters, "counters", torch.int32, 1)
+    if counters.numel() < decode_counter_bytes(B, H, H_kv) // 4:
+        raise ValueError("counters too small")
+    out = torch.full((1,), -1, dtype=torch.int32, device=counters.device)
+    _check("fa_decode_counters_check",
+           library().fa_decode_counters_check(counters.data_ptr(), B, H, H_kv, out.data_ptr(), _stream_ptr(counters)))
+    return int(out.item())
 
 
 def decode_static(q, k, v, num_splits: int | None = None, scale: float | None = None, out=None, lse=None):

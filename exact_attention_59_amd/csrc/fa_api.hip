@@ -362,6 +362,27 @@ FA_EXPORT int fa_decode_static(const void* Q, const void* K, const void* V, void
                   "fa_decode_static");
 }
 
+FA_EXPORT int fa_decode_counters_reset(int* counters, int B, int H, int H_kv, void* stream) {
+    if (!counters) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv) return FA_ERR_SHAPE;
+    const long long n = (long long)B * H_kv * ((H / H_kv + fa::kDecHeadsPerBlock - 1) / fa::kDecHeadsPerBlock);
+    if (n > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(counters) & 3u) return FA_ERR_ALIGN;
+    return finish(fa::launch_counters_reset(counters, (int)n, static_cast<hipStream_t>(stream)),
+                  "fa_decode_counters_reset");
+}
+
+FA_EXPORT int fa_decode_counters_check(const int* counters, int B, int H, int H_kv, int* nonzero, void* stream) {
+    if (!counters || !nonzero) return FA_ERR_NULL;
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv) return FA_ERR_SHAPE;
+    const long long n = (long long)B * H_kv * ((H / H_kv + fa::kDecHeadsPerBlock - 1) / fa::kDecHeadsPerBlock);
+    if (n > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(counters) & 3u) || (reinterpret_cast<uintptr_t>(nonzero) & 3u))
+        return FA_ERR_ALIGN;
+    return finish(fa::launch_counters_check(counters, (int)n, nonzero, static_cast<hipStream_t>(stream)),
+                  "fa_decode_counters_check");
+}
+
 FA_EXPORT size_t fa_decode_counter_bytes(int B, int H, int H_kv) {
     if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv) return 0;
     const size_t n_qc = (size_t)(H / H_kv + fa::kDecHeadsPerBlock - 1) / fa::kDecHeadsPerBlock;

@@ -566,6 +566,18 @@ __global__ void zero_ints_kernel(int* p, int n) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// Number of non-zero ints among p[0 .. n) into *out (one workgroup).
+__global__ __launch_bounds__(256) void count_nonzero_kernel(const int* p, int n, int* out) {
+    __shared__ int total;
+    if (threadIdx.x == 0) total = 0;
+    __syncthreads();
+    int c = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) c += p[i] != 0;
+    atomicAdd(&total, c);
+    __syncthreads();
+    if (threadIdx.x == 0) *out = total;
+}
+
 constexpr int kMaxDevices = 64;
 
 // Device address of this device's scratch array, looked up once per device (with that
@@ -617,6 +629,16 @@ hipError_t launch_decode_static(const void* Q, const void* K, const void* V, voi
     float* o_part = reinterpret_cast<float*>(base + kStaticCounterBytes + (rows * sizeof(float) + 255) / 256 * 256);
     return launch_decode_fused(Q, K, V, o_part, lse_part, counters, O, LSE, B, H, H_kv, N_k, d, num_splits, scale,
                                stream);
+}
+
+hipError_t launch_counters_reset(int* counters, int n, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)min((n + 255) / 256, 64)), dim3(256), 0, stream, counters, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_counters_check(const int* counters, int n, int* nonzero, hipStream_t stream) {
+    hipLaunchKernelGGL(count_nonzero_kernel, dim3(1), dim3(256), 0, stream, counters, n, nonzero);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_split(const void* Q, const void* K, const void* V, float* O_part,

@@ -63,6 +63,10 @@ hipError_t launch_decode_fused(const void* Q, const void* K, const void* V, floa
                                int* counters, void* O, float* LSE, int B, int H, int H_kv, int N_k, int d,
                                int num_splits, float scale, hipStream_t stream);
 
+// Group counters of the one-launch decode: zero them, or count the non-zero ones into *nonzero.
+hipError_t launch_counters_reset(int* counters, int n, hipStream_t stream);
+hipError_t launch_counters_check(const int* counters, int n, int* nonzero, hipStream_t stream);
+
 // fa_decode_static: fa_decode with its workspace and counters in a file-scope device array
 // of kStaticScratchBytes (no allocation); the first call on a device clears its counters.
 constexpr size_t kStaticScratchBytes = (size_t)16 << 20;

@@ -212,6 +212,26 @@ def test_decode_static_capacity_boundary(lib):
     assert dec_static(lib, L=None, scale=0.0) == fa.FA_ERR_ARG
 
 
+@pytest.mark.parametrize("fn", ["reset", "check"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=None), fa.FA_ERR_NULL), (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=6, H_kv=4), fa.FA_ERR_SHAPE),
+    (dict(C=ctypes.c_void_p(0x100002)), fa.FA_ERR_ALIGN),
+])
+def test_decode_counters_helpers_validation(lib, fn, kw, status):
+    a = dict(C=P, B=2, H=8, H_kv=2)
+    a.update(kw)
+    if fn == "reset":
+        st = lib.fa_decode_counters_reset(a["C"], a["B"], a["H"], a["H_kv"], None)
+    else:
+        st = lib.fa_decode_counters_check(a["C"], a["B"], a["H"], a["H_kv"], P, None)
+    assert st == status
+
+
+def test_decode_counters_check_needs_its_output(lib):
+    assert lib.fa_decode_counters_check(P, 2, 8, 2, None, None) == fa.FA_ERR_NULL
+    assert lib.fa_decode_counters_check(P, 2, 8, 2, ctypes.c_void_p(0x100001), None) == fa.FA_ERR_ALIGN
+
+
 def test_decode_counter_bytes(lib):
     assert fa.decode_counter_bytes(4, 32, 8) == 4 * 8 * 1 * 4
     assert fa.decode_counter_bytes(2, 40, 2) == 2 * 2 * 2 * 4   # 20 query heads per K/V head: two chunks of 16

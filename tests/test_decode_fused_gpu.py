@@ -83,8 +83,10 @@ def test_decode_fused_calls_share_counters(orc):
         check_fused(orc, "fused decode call %d N_k=%d S=%d" % (i, N_k, S), Q, K, V, S, counters=counters)
 
 
-@pytest.mark.parametrize("N_k,seed", [(4096, 5)])
+@pytest.mark.parametrize("N_k,seed", [(4096, 5), (65536, 6)])
 def test_decode_fused_full_workload(orc, N_k, seed):
+    """Both cache lengths of the flash-decoding workload, at the split count the library picks
+    (the long cache's partials are checked on sampled segments, check_fused)."""
     B, H, H_kv, d = 4, 32, 8, 128
     S = fa.decode_num_splits(B, H_kv, N_k, d)
     name = "fused flash-decoding B=4 H=32/8 N_k=%d d=128 S=%d" % (N_k, S)
@@ -109,7 +111,10 @@ def test_decode_fused_is_deterministic():
     say("fused decode determinism", (B, H, H_kv, N_k, d))
     Q, K, V = decode_inputs(17, B, H, H_kv, N_k, d)
     q, k, v = to_dev(Q[:, :, 0, :]), to_dev(K), to_dev(V)
-    S = fa.decode_num_splits(B, H_kv, N_k, d)
+    # S fixed (not the CU-count heuristic): the paged path rounds segments up to 32-key blocks, so
+    # paged and contiguous segments coincide only when N_k / S is a multiple of 32
+    S = 16
+    assert (N_k // S) % 32 == 0 and N_k % S == 0
     runs = [fa.decode(q, k, v, S) for _ in range(3)]
     torch.cuda.synchronize()
     for o, l in runs[1:]:
@@ -129,3 +134,26 @@ def test_decode_fused_is_deterministic():
         assert torch.equal(l.view(torch.int32), pruns[0][1].view(torch.int32))
     # paged and contiguous: the same keys in the same segments, so the same bits
     assert torch.equal(pruns[0][0].view(torch.int16), runs[0][0].view(torch.int16))
+
+
+def test_poisoned_counters_are_reported_not_used(orc):
+    """A counter array that is not zero on entry is reported (fa_decode_counters_check), the
+    checked binding refuses to launch on it, and fa_decode_counters_reset makes it usable."""
+    B, H, H_kv, N_k, d, S = 2, 8, 2, 1000, 128, 7
+    Q, K, V = decode_inputs(7401, B, H, H_kv, N_k, d)
+    q, k, v = to_dev(Q[:, :, 0, :]), to_dev(K), to_dev(V)
+    n = fa.decode_counter_bytes(B, H, H_kv) // 4
+    counters = torch.zeros(n, dtype=torch.int32, device="cuda")
+    assert fa.decode_counters_check(counters, B, H, H_kv) == 0
+    counters[0] = 3  # as if a group had been counted and never cleared
+    counters[-1] = -1
+    assert fa.decode_counters_check(counters, B, H, H_kv) == (2 if n > 1 else 1)
+    with pytest.raises(RuntimeError, match="not zero"):
+        fa.decode(q, k, v, S, counters=counters, check_counters=True)
+    fa.decode_counters_reset(counters, B, H, H_kv)
+    assert fa.decode_counters_check(counters, B, H, H_kv) == 0
+    o, l = fa.decode(q, k, v, S, counters=counters, check_counters=True)
+    torch.cuda.synchronize()
+    O_ref, L_ref = orc.attention(Q, K, V)
+    check("decode after counters reset", bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
+    assert fa.decode_counters_check(counters, B, H, H_kv) == 0

@@ -176,3 +176,26 @@ def test_paged_one_launch(orc, shared_paged_counters, B, H, H_kv, lens, d, P, S)
 def shared_paged_counters():
     n = max(fa.decode_counter_bytes(B, H, H_kv) for B, H, H_kv, _, _, _, _ in PAGED) // 4
     return torch.zeros(n, dtype=torch.int32, device="cuda:0")
+
+
+def test_paged_full_long_cache(orc):
+    """The flash-decoding workload's long cache (B=4, H=32, H_kv=8, N_k=65536, d=128) scattered
+    over a shuffled pool of 16-token pages: the paged split + combine and the one-launch
+    fa_decode_paged against the oracle on the contiguous cache."""
+    B, H, H_kv, N_k, d, P = 4, 32, 8, 65536, 128, 16
+    S = fa.decode_num_splits(B, H_kv, N_k, d)
+    name = "paged flash-decoding B=4 H=32/8 N_k=65536 d=128 page=16 S=%d" % S
+    say(name)
+    Q, K, V = decode_inputs(6, B, H, H_kv, N_k, d)
+    lens = [N_k] * B
+    Kp, Vp, table = make_paged(K, V, lens, P, seed=66, spare=2)
+    O_ref, L_ref = orc.attention(Q, K, V)
+    o_part, l_part, o, l = run_paged(Q, Kp, Vp, table, lens, S)
+    check(name + " split + combine", bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
+    q = to_dev(Q[:, :, 0, :])
+    kp, vp = to_dev(Kp), to_dev(Vp)
+    t = torch.from_numpy(table).cuda()
+    ln = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    o1, l1 = fa.decode_paged(q, kp, vp, t, ln, S)
+    torch.cuda.synchronize()
+    check(name + " one launch", bf16_dev_to_f64(o1), O_ref[:, :, 0], l1.cpu().numpy(), L_ref[:, :, 0])
