@@ -233,12 +233,13 @@ def check_fp8(name, O_gpu, O_q, L_gpu, L_q, O_x=None, L_x=None, lse_slack=None):
 
 
 def mfma_fp8_score_bound(qd, kd, scale, rows_per_chunk=64):
-    """Per query row, a bound on the score error of gfx950's fp8 matrix cores (measured by an
-    on-GPU probe: within each group of 8 consecutive contraction slots -- 8 consecutive
-    channels here -- every product is truncated toward zero to a multiple of 2^(e - 14), e the
-    exponent of the group's largest product, so the group loses less than 7 * 2^-14 times
-    its largest product).  qd [B,H,N_q,d], kd [B,H_kv,N_k,d] dequantised (float64); returns
-    [B,H,N_q]: scale * 7 * 2^-14 * max over keys of sum over groups of max |q_k k_k|, which
+    """Per query row, a bound on the score error of gfx950's fp8 matrix cores.  Within each group
+    of 8 consecutive contraction slots (8 consecutive channels here) every product is truncated
+    toward zero to a multiple of 2^(E - 13), E the group's largest exponent(q) + exponent(k)
+    (pinned by test_fp8_gpu.py::test_fp8_matrix_core_product_truncation).  The group's largest
+    product is at least 2^E and is not truncated, so the group loses less than 7 * 2^-13 times
+    its largest product.  qd [B,H,N_q,d], kd [B,H_kv,N_k,d] dequantised (float64); returns
+    [B,H,N_q]: scale * 7 * 2^-13 * max over keys of sum over groups of max |q_k k_k|, which
     bounds the row's LSE error from this source."""
     B, H, N_q, d = qd.shape
     H_kv = kd.shape[1]
@@ -250,7 +251,7 @@ def mfma_fp8_score_bound(qd, kd, scale, rows_per_chunk=64):
                 q = np.abs(qd[b, h, r0:r0 + rows_per_chunk]).reshape(-1, 1, d // 8, 8)
                 g = (q * k[None]).max(axis=-1).sum(axis=-1)  # [rows, N_k]
                 out[b, h, r0:r0 + rows_per_chunk] = g.max(axis=-1)
-    return scale * 7.0 * 2.0 ** -14 * out
+    return scale * 7.0 * 2.0 ** -13 * out
 
 
 def gpu_available():
