@@ -49,16 +49,28 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attn fwd TFLOPS & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 SQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
-KERNEL_SOURCES = ["fa_common.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_decode.hip"]
+# The sources each kernel family is compiled from: a counter summary stays valid for a kernel
+# while these hash the same.
+KERNEL_SOURCES = {"fwd_kernel": ["fa_common.hpp", "fa_launch.hpp", "fa_fwd.hip"],
+                  "fwd_fp8_kernel": ["fa_common.hpp", "fa_launch.hpp", "fa_fp8.hip"],
+                  "fp8_quant_kernel": ["fa_common.hpp", "fa_launch.hpp", "fa_fp8.hip"],
+                  "bwd": ["fa_common.hpp", "fa_launch.hpp", "fa_bwd.hip"],
+                  "decode_split_kernel": ["fa_common.hpp", "fa_launch.hpp", "fa_decode.hip"],
+                  "combine_kernel": ["fa_common.hpp", "fa_launch.hpp", "fa_decode.hip"]}
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources `kernel` (a name such as "fwd_kernel<128, true>") is built from."""
+    family = kernel.split("<")[0].strip()
+    family = "bwd" if family.startswith("bwd_") else family
+    if family not in KERNEL_SOURCES:
+        raise KeyError("no source list for kernel %r" % kernel)
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "exact_attention_59_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -450,10 +462,10 @@ def traffic_from_counters(dominant_kernel_substr):
             c = json.load(f)
     except (OSError, ValueError):
         return None, "no counter summary"
-    if c.get("kernel_source_hash") != kernel_source_hash():
-        return None, "kernels changed since the counters were taken"
     for name, k in c.get("kernels", {}).items():
         if dominant_kernel_substr in name:
+            if k.get("source_hash") != kernel_source_hash(name):
+                return None, "kernel changed since the counters were taken"
             return k.get("hbm_bytes_per_launch"), "profiles/hbm_counters.json (%s)" % name
     return None, "dominant kernel not in the counter summary"
 
@@ -466,10 +478,10 @@ def shader_counters(dominant_kernel_substr):
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
-        return None
     for name, k in c.get("kernels", {}).items():
         if dominant_kernel_substr in name:
+            if k.get("source_hash") != kernel_source_hash(name):
+                return None
             return dict(k, source="profiles/sq_counters.json (%s)" % name)
     return None
 

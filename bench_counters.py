@@ -3,9 +3,9 @@
 
     cd /tmp && export TMPDIR=/tmp
     rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/fetch -o run -- \\
-        python3 <repo>/bench.py --legs fwd,decode,copy --steps 3 --warmup 1 --decode-reps 3
+        python3 <repo>/bench.py --legs fwd,fwd_other,decode,copy --steps 3 --warmup 1 --decode-reps 3
     rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/write -o run -- \\
-        python3 <repo>/bench.py --legs fwd,decode,copy --steps 3 --warmup 1 --decode-reps 3
+        python3 <repo>/bench.py --legs fwd,fwd_other,decode,copy --steps 3 --warmup 1 --decode-reps 3
     python3 <repo>/bench_counters.py OUT/fetch OUT/write
     # or, with several runs (decode kernels of different cache lengths share one grid):
     python3 <repo>/bench_counters.py N_k=4096=OUT/f4096,OUT/w4096 N_k=65536=OUT/f65536,OUT/w65536
@@ -13,7 +13,7 @@
     # shader counters (MFMA and VALU activity, LDS bank conflicts) of one run:
     rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA SQ_INSTS_VALU \
         SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d OUT/sq -o run -- \
-        python3 <repo>/bench.py --legs fwd,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3
+        python3 <repo>/bench.py --legs fwd,fwd_other,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3
     python3 <repo>/bench_counters.py sq OUT/sq        # -> profiles/sq_counters.md and .json
     # kernel durations of a plain bench run:
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- python3 <repo>/bench.py
@@ -25,7 +25,7 @@ FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the L2 channels) are sc
 what the same counters read for the bench's plain 1 GiB device copy (`--legs copy`):
 factor = known bytes / counted bytes, separately for reads and writes.  The result goes
 to profiles/hbm_counters.json (read by bench.py, which reports it as roofline.traffic
-only while the kernel sources still hash the same) and profiles/hbm_counters.md.
+only while that kernel's sources still hash the same) and profiles/hbm_counters.md.
 """
 from __future__ import annotations
 
@@ -66,8 +66,7 @@ def read_counter(run_dir: str, counter: str, label: str = "", per=None) -> dict:
             key = kernel_key(row["Kernel_Name"])
             if key:
                 key += " grid=%s" % row["Grid_Size"]
-                # the prefill launches are the same in every run; the rest depend on N_k
-                if label and not key.startswith(("copy", "fwd_kernel<64")):
+                if label and not key.startswith("copy"):
                     key += " " + label
                 per[key][(f, row["Dispatch_Id"])] += float(row["Counter_Value"])
     return per
@@ -75,6 +74,27 @@ def read_counter(run_dir: str, counter: str, label: str = "", per=None) -> dict:
 
 def averages(per) -> dict:
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def merge_unchanged(fetch: dict, write: dict, labels: list, tol: float = 0.03):
+    """Kernels whose launches read and write the same (within `tol`) in every labelled run
+    (the prefill legs, which do not depend on the decode cache length) are listed once,
+    without a label; the others keep one entry per run."""
+    labels = [l for l in labels if l]
+    if len(labels) < 2:
+        return fetch, write
+    bases = {k[: -len(" " + l)] for k in fetch for l in labels if k.endswith(" " + l)}
+    for base in bases:
+        keys = [base + " " + l for l in labels]
+        if not all(k in fetch and k in write for k in keys):
+            continue
+        same = all(max(d[k] for k in keys) <= (1 + tol) * min(d[k] for k in keys) for d in (fetch, write))
+        if same:
+            for d in (fetch, write):
+                d[base] = sum(d[k] for k in keys) / len(keys)
+                for k in keys:
+                    del d[k]
+    return fetch, write
 
 
 SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
@@ -96,6 +116,8 @@ def sq_summary(run_dir: str, cmd: str) -> str:
             if m:
                 key = "%s grid=%s" % (m.group(1), row["Grid_Size"])
                 per[key][row["Counter_Name"]][(f, row["Dispatch_Id"])] += float(row["Counter_Value"])
+    import bench
+
     names = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_MFMA",
              "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
     lines = ["# Shader counters per kernel launch (rocprofv3 SQ counters, averages per dispatch)", "",
@@ -110,7 +132,7 @@ def sq_summary(run_dir: str, cmd: str) -> str:
     for key in sorted(per):
         avg = {n: (sum(per[key][n].values()) / len(per[key][n])) if per[key][n] else float("nan") for n in names}
         gpu = avg["GRBM_GUI_ACTIVE"] / XCDS
-        table[key] = {"gpu_cycles": round(gpu), "mfma_busy_pct": round(100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS), 2)
+        table[key] = {"source_hash": bench.kernel_source_hash(key), "gpu_cycles": round(gpu), "mfma_busy_pct": round(100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS), 2)
                       if gpu else None, "lds_instr": round(avg["SQ_INSTS_LDS"]),
                       "lds_bank_conflicts": round(avg["SQ_LDS_BANK_CONFLICT"])}
         lines.append("| %s | %.0f | %.1f | %.1f | %.0f | %.0f | %.0f | %.0f | %.4f |" % (
@@ -150,6 +172,21 @@ def trace_summary(run_dir: str, cmd: str, tail: int = 200) -> str:
         if not re.search(SQ_KERNELS, k):
             continue
         out.append("| %s | %d | %.2f | %.2f | %.2f |" % (k, len(v), sum(v) / len(v), min(v), sum(v[-tail:]) / len(v[-tail:])))
+    # the headline step's kernel: its rate from this trace, to compare with bench.py's roofline line
+    import bench
+
+    w = bench.HEADLINE
+    t_r = -(-w["N"] // 128)
+    grid = ((t_r + 1) // 2 if w["causal"] else t_r) * w["B"] * w["H"] * 256
+    key = "fwd_kernel<%d, %s> grid=%d" % (w["d"], "true" if w["causal"] else "false", grid)
+    if key in g:
+        v = g[key][-tail:]
+        us = sum(v) / len(v)
+        fl = bench.fwd_flops(w["B"], w["H"], w["N"], w["N"], w["d"], w["causal"])
+        out += ["", "Headline step (%s): %s averages %.2f us over its last %d launches, so %.1f TFLOP/s = %.4f of "
+                "the %.1f TFLOP/s bf16 peak (bench.py's roofline.frac comes from HIP events around the same "
+                "launches)." % (w["name"], key, us, len(v), fl / us / 1e6, fl / us / 1e6 / bench.PEAK_BF16_TFLOPS,
+                                bench.PEAK_BF16_TFLOPS)]
     return "\n".join(out) + "\n"
 
 
@@ -190,14 +227,12 @@ def main():
     if len(args) == 2 and args[0] == "sq":
         cmd = ("rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA SQ_INSTS_VALU "
                "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d OUT/sq -o run -- "
-               "python3 <repo>/bench.py --legs fwd,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3")
+               "python3 <repo>/bench.py --legs fwd,fwd_other,bwd,fp8,decode --decode-nk 65536 --steps 3 --warmup 1 --decode-reps 3")
         text, table = sq_summary(args[1], cmd)
         with open(os.path.join(ROOT, "profiles", "sq_counters.md"), "w") as f:
             f.write(text)
-        import bench
-
         with open(os.path.join(ROOT, "profiles", "sq_counters.json"), "w") as f:
-            json.dump({"kernel_source_hash": bench.kernel_source_hash(), "command": cmd, "kernels": table}, f, indent=1)
+            json.dump({"command": cmd, "kernels": table}, f, indent=1)
         print(text)
         return
     if len(args) == 2 and "=" not in args[0]:
@@ -216,7 +251,7 @@ def main():
     for label, f_dir, w_dir in runs:
         fetch_per = read_counter(f_dir, "FETCH_SIZE", label, fetch_per)
         write_per = read_counter(w_dir, "WRITE_SIZE", label, write_per)
-    fetch, write = averages(fetch_per), averages(write_per)
+    fetch, write = merge_unchanged(averages(fetch_per), averages(write_per), [lab for lab, _, _ in runs])
     # The calibration copy is the 1 GiB one.  Other copies of the bench's set-up (the decode
     # leg's rotated cache copies, at most 537 MB each, share the copy kernel's grid; torch
     # copy kernels also match the name) are smaller, so the calibration takes the copy
@@ -235,15 +270,15 @@ def main():
     for k in sorted(set(fetch) & set(write)):
         if k.startswith("copy"):
             continue
-        kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+        kernels[k] = {"source_hash": bench.kernel_source_hash(k), "fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
                       "hbm_read_bytes_per_launch": round(fetch[k] * 1024 * f_read),
                       "hbm_write_bytes_per_launch": round(write[k] * 1024 * f_write),
                       "hbm_bytes_per_launch": round(fetch[k] * 1024 * f_read + write[k] * 1024 * f_write)}
-    out = {"kernel_source_hash": bench.kernel_source_hash(), "copy_bytes": COPY_BYTES,
+    out = {"copy_bytes": COPY_BYTES,
            "copy_fetch_kib": round(fetch["copy"], 1), "copy_write_kib": round(write["copy"], 1),
            "factor_read": round(f_read, 4), "factor_write": round(f_write, 4), "kernels": kernels,
            "command": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --kernel-trace --output-format csv -- "
-                      "python3 bench.py --legs fwd,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3"}
+                      "python3 bench.py --legs fwd,fwd_other,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3"}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "hbm_counters.json"), "w") as f:
         json.dump(out, f, indent=1)
@@ -251,15 +286,16 @@ def main():
              "Commands (run from /tmp with TMPDIR=/tmp, one counter per run, for each cache length NK "
              "of the decode leg):", "",
              "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d OUT/FETCH_SIZE_NK -o run -- "
-             "python3 <repo>/bench.py --legs fwd,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3",
+             "python3 <repo>/bench.py --legs fwd,fwd_other,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3",
              "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d OUT/WRITE_SIZE_NK -o run -- "
-             "python3 <repo>/bench.py --legs fwd,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3",
+             "python3 <repo>/bench.py --legs fwd,fwd_other,decode,copy --decode-nk NK --steps 3 --warmup 1 --decode-reps 3",
              "    python3 <repo>/bench_counters.py " + " ".join(
                  "%s=OUT/FETCH_SIZE_%s,OUT/WRITE_SIZE_%s" % (lab, lab.split("=")[-1], lab.split("=")[-1])
                  if lab else "OUT/fetch OUT/write" for lab, _, _ in runs), "",
              "Calibration: the bench's 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB, "
              "so counted reads are scaled by %.4f and writes by %.4f." % (fetch["copy"], write["copy"], f_read, f_write),
-             "Kernel sources hash: `%s`." % out["kernel_source_hash"], "",
+             "Each kernel's entry in hbm_counters.json carries the hash of the sources it is built from; "
+             "bench.py reports its traffic only while they hash the same.", "",
              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |", "|---|---|---|---|---|"]
     for k, v in kernels.items():
         lines.append("| %s | %.0f | %.0f | %.2f | %.2f |" % (k, v["fetch_kib"], v["write_kib"],
