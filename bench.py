@@ -19,7 +19,9 @@ uses of a copy, beyond the 256 MB last-level cache); per-repetition timings, wit
 read sweep before each repetition, are reported beside it and for the combine.  The backward leg
 (fa_bwd on the batched-prefill shape) is reported under "backward", in TFLOP/s of its five
 N_q x N_k x d products.  The FP8 leg (quantiser + e4m3 forward) is reported under "fp8",
-against the 5.03 PFLOP/s dense fp8 peak.
+against the 5.03 PFLOP/s dense fp8 peak.  The poly leg times fa_fwd_poly_exp2 (a quarter, half
+or all of the softmax exponentials by a cubic on the FMA units) against fa_fwd, under
+"fwd_poly_exp2".
 
 Inputs are synthetic and seeded (counter-based SplitMix64 + Box-Muller, see gen/),
 already resident in device memory when timing starts.  GPU times come from HIP
@@ -151,7 +153,7 @@ def leg_forward(fa, torch, steps, warmup, name, seed, B, H, H_kv, N, d, causal):
     }
 
 
-def leg_forward_other(fa, torch, reps, name, seed, B, H, H_kv, N, d, causal):
+def leg_forward_other(fa, torch, reps, name, seed, B, H, H_kv, N, d, causal, poly_exp2=0):
     Q, K, V = fwd_inputs(seed, B, H, H_kv, N, d)
     q, k, v = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
     o = torch.empty_like(q)
@@ -159,12 +161,12 @@ def leg_forward_other(fa, torch, reps, name, seed, B, H, H_kv, N, d, causal):
     # Warm up for at least 30 ms of GPU time, so the clock has settled (it dips for about
     # 10 ms after sustained load starts) before the timed launches; then `reps` back-to-back
     # launches between one event pair.
-    settle(torch, lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
+    settle(torch, lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse, poly_exp2=poly_exp2))
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        fa.fwd(q, k, v, causal=causal, out=o, lse=lse, poly_exp2=poly_exp2)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
@@ -492,9 +494,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
-    ap.add_argument("--legs", default="fwd,fwd_other,decode,bwd,fp8,cpu",
+    ap.add_argument("--legs", default="fwd,fwd_other,decode,bwd,fp8,poly,cpu",
                     help="comma list of fwd (the headline step), fwd_other (the batched-prefill and grouped-query "
-                         "forward workloads), decode, bwd, fp8, cpu, copy")
+                         "forward workloads), decode, bwd, fp8, poly (the forward with polynomial exponentials), "
+                         "cpu, copy")
     ap.add_argument("--all", action="store_true", help="add fwd_other to --legs")
     ap.add_argument("--decode-reps", type=int, default=30)
     ap.add_argument("--decode-nk", default="4096,65536", help="comma list of decode cache lengths")
@@ -561,6 +564,22 @@ def main():
             out["forward_workloads"].append({k: (round(v, 2) if isinstance(v, float) else v) for k, v in
                                              leg_forward_other(fa, torch, 50, name, seed, B, H, H_kv, N, d,
                                                                causal).items()})
+            torch.cuda.empty_cache()
+
+    if "poly" in legs:
+        # fa_fwd_poly_exp2: a quarter, half or all of the softmax exponentials on the FMA units
+        out["fwd_poly_exp2"] = []
+        for name, seed, B, H, H_kv, N, d, causal in (
+                ("batched prefill B=16 H=16 N=1024 d=64 non-causal", 2, 16, 16, 16, 1024, 64, False),
+                ("long causal B=2 H=16 N=8192 d=128", 3, 2, 16, 16, 8192, 128, True)):
+            base = leg_forward_other(fa, torch, 50, name, seed, B, H, H_kv, N, d, causal)
+            rec = {"workload": name, "exact_exp2_us": round(base["us"], 2)}
+            for qu in (1, 2, 4):
+                r = leg_forward_other(fa, torch, 50, name, seed, B, H, H_kv, N, d, causal, poly_exp2=qu)
+                rec["poly_%d_of_4_us" % qu] = round(r["us"], 2)
+                rec["poly_%d_of_4_vs_exact" % qu] = round(r["us"] / base["us"], 3)
+            log("poly exp2", rec)
+            out["fwd_poly_exp2"].append(rec)
             torch.cuda.empty_cache()
 
     if "decode" in legs:

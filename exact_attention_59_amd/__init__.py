@@ -51,6 +51,8 @@ def library():
         lib = ctypes.CDLL(LIBRARY)
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.fa_fwd_poly_exp2.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+        lib.fa_exp2_poly.argtypes = [vp, vp, ctypes.c_longlong, vp]
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
         lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -128,8 +130,10 @@ def _need(t, name, dtype, ndim):
         raise ValueError("%s must be contiguous" % name)
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """fa_fwd.  q [B,H,N_q,d], k/v [B,H_kv,N_k,d] bf16 -> o [B,H,N_q,d] bf16, lse [B,H,N_q] fp32."""
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, poly_exp2: int = 0):
+    """fa_fwd.  q [B,H,N_q,d], k/v [B,H_kv,N_k,d] bf16 -> o [B,H,N_q,d] bf16, lse [B,H,N_q] fp32.
+    poly_exp2 in (1, 2, 4): fa_fwd_poly_exp2 with that many of every four softmax exponentials
+    taken by the FMA-unit polynomial (0: fa_fwd)."""
     torch = _torch()
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
@@ -148,9 +152,26 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     _need(lse, "lse", torch.float32, 3)
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, N_q):
         raise ValueError("output shapes do not match q")
-    _check("fa_fwd", library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                      B, H, H_kv, N_q, N_k, d, int(bool(causal)), float(scale), _stream_ptr(q)))
+    if poly_exp2:
+        _check("fa_fwd_poly_exp2", library().fa_fwd_poly_exp2(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, N_q, N_k, d,
+            int(bool(causal)), float(scale), int(poly_exp2), _stream_ptr(q)))
+    else:
+        _check("fa_fwd", library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                          B, H, H_kv, N_q, N_k, d, int(bool(causal)), float(scale), _stream_ptr(q)))
     return out, lse
+
+
+def exp2_poly(x, out=None):
+    """fa_exp2_poly: y = 2^x with the forward's polynomial (x: fp32 CUDA tensor, any shape)."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    out = torch.empty_like(x) if out is None else out
+    if out.dtype != torch.float32 or out.shape != x.shape or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous float32 tensor shaped like x")
+    _check("fa_exp2_poly", library().fa_exp2_poly(x.data_ptr(), out.data_ptr(), x.numel(), _stream_ptr(x)))
+    return out
 
 
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,

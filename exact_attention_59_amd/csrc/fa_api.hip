@@ -89,8 +89,9 @@ FA_EXPORT long long fa_fwd_tile_count(int N_q, int N_k, int d, int causal) {
     return total;
 }
 
-FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
-                     int N_q, int N_k, int d, int causal, float scale, void* stream) {
+// Checks shared by the two forward entry points; *blocks gets the launch's workgroup count.
+static int check_fwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, int B, int H,
+                     int H_kv, int N_q, int N_k, int d, int causal, float scale, long long* blocks_out) {
     if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
     if (B <= 0 || H <= 0 || H_kv <= 0 || N_q <= 0 || N_k <= 0 || d <= 0) return FA_ERR_SHAPE;
     if (H % H_kv) return FA_ERR_SHAPE;
@@ -102,12 +103,44 @@ FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float
     if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(LSE)) return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    *blocks_out = blocks;
+    return FA_OK;
+}
+
+FA_EXPORT int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
+                     int N_q, int N_k, int d, int causal, float scale, void* stream) {
+    long long blocks = 0;
+    const int st = check_fwd(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal, scale, &blocks);
+    if (st != FA_OK) return st;
     if (debug_enabled())
         fprintf(stderr, "[fa] fwd B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d causal=%d blocks=%lld\n", B, H, H_kv, N_q,
                 N_k, d, causal, blocks);
     return finish(fa::launch_fwd(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal == 1, scale,
                                  static_cast<hipStream_t>(stream)),
                   "fa_fwd");
+}
+
+FA_EXPORT int fa_fwd_poly_exp2(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                               int H_kv, int N_q, int N_k, int d, int causal, float scale, int poly_quarters,
+                               void* stream) {
+    long long blocks = 0;
+    const int st = check_fwd(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal, scale, &blocks);
+    if (st != FA_OK) return st;
+    if (poly_quarters != 1 && poly_quarters != 2 && poly_quarters != 4) return FA_ERR_ARG;
+    if (debug_enabled())
+        fprintf(stderr, "[fa] fwd_poly_exp2 B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d causal=%d quarters=%d\n", B, H,
+                H_kv, N_q, N_k, d, causal, poly_quarters);
+    return finish(fa::launch_fwd_poly(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal == 1, scale, poly_quarters,
+                                      static_cast<hipStream_t>(stream)),
+                  "fa_fwd_poly_exp2");
+}
+
+FA_EXPORT int fa_exp2_poly(const float* x, float* y, long long n, void* stream) {
+    if (!x || !y) return FA_ERR_NULL;
+    if (n < 0) return FA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(y) & 3u)) return FA_ERR_ALIGN;
+    if (n == 0) return FA_OK;
+    return finish(fa::launch_exp2_poly(x, y, n, static_cast<hipStream_t>(stream)), "fa_exp2_poly");
 }
 
 FA_EXPORT int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,

@@ -85,6 +85,25 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // log2(x) on the transcendental unit (v_log_f32).
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// 2^x on the FMA units (FA4's softmax trick: part of the exponentials leave the
+// transcendental unit; CUDA Kernel interview course, FlashAttention v4 card).  Reduction
+// x = n + f with n = floor(x) and f = x - n in [0, 1] (the subtraction is exact, except that a
+// tiny negative x rounds f to 1), the cubic p(f) = 1 + f (c1 + c2 f + c3 f^2)
+// whose fp32 coefficients minimise max |p(f) / 2^f - 1| on [0, 1] (Remez exchange; printed by
+// exact_attention_59_amd/fit_exp2_poly.py), then ldexp by n.  Relative error <= 8.6e-5 for
+// x >= -126, and exact at integers (p(0) = 1); arguments at or below -200, and -inf, give
+// exactly 0 (ldexp underflows), those in (-200, -126) a value below 2^-126.  Eight VALU
+// instructions against one transcendental one.
+constexpr float kExp2C1 = 0x1.63e658p-1f, kExp2C2 = 0x1.d2378ap-3f, kExp2C3 = 0x1.3baaa6p-4f;
+__device__ __forceinline__ float exp2_poly(float x) {
+    x = fmaxf(x, -200.f);
+    const float fl = floorf(x);
+    const float f = x - fl;
+    const int n = (int)fl;
+    const float p = fmaf(fmaf(fmaf(kExp2C3, f, kExp2C2), f, kExp2C1), f, 1.f);
+    return __builtin_ldexpf(p, n);
+}
+
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, kWave)); }
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, kWave); }
 

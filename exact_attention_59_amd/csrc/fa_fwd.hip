@@ -35,6 +35,7 @@
 // Softmax in base 2: t = s * scale * log2(e); m is kept in t units;
 // p = 2^(t - m), alpha = 2^(m_old - m_new); LSE = (m + log2 l) * ln 2.
 // l sums the fp32 p (before rounding P to bf16).
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -76,7 +77,9 @@ constexpr float kRescaleSlack = 8.0f;
 template <int D>
 constexpr int kFwdBlocksPerCU = D == 64 ? 3 : 2;
 
-template <int D, bool CAUSAL>
+// POLY (0..4): of every four exponentials of a lane's softmax, the first POLY are taken with
+// exp2_poly on the FMA units and the rest with v_exp_f32 (0 = all on the transcendental unit).
+template <int D, bool CAUSAL, int POLY = 0>
 __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V,
@@ -303,7 +306,8 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
         for (int mb = 0; mb < BC / 32; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = exp2_hw(fmaf(s[mb][r], c, -m_use));
+                const float x = fmaf(s[mb][r], c, -m_use);
+                const float p = (r & 3) < POLY ? exp2_poly(x) : exp2_hw(x);
                 s[mb][r] = p;
                 ps += p;
             }
@@ -408,14 +412,14 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int POLY = 0>
 hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
                         int H_kv, int N_q, int N_k, float scale, hipStream_t stream) {
     const int T_r = (N_q + kFwdBlockRows - 1) / kFwdBlockRows;
     const int BH = B * H;
     const float c = (float)((double)scale * 1.4426950408889634073599);
     const long long blocks = (long long)(CAUSAL ? (T_r + 1) / 2 : T_r) * BH;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                        static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), LSE, H, H_kv, N_q, N_k,
                        T_r, BH, c);
@@ -431,6 +435,41 @@ hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, floa
                       : launch_fwd_t<64, false>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, scale, stream);
     return causal ? launch_fwd_t<128, true>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, scale, stream)
                   : launch_fwd_t<128, false>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, scale, stream);
+}
+
+template <int POLY>
+hipError_t launch_fwd_poly_t(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                             int H_kv, int N_q, int N_k, int d, bool causal, float scale, hipStream_t stream) {
+    if (d == 64)
+        return causal ? launch_fwd_t<64, true, POLY>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, scale, stream)
+                      : launch_fwd_t<64, false, POLY>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, scale, stream);
+    return causal ? launch_fwd_t<128, true, POLY>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, scale, stream)
+                  : launch_fwd_t<128, false, POLY>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, scale, stream);
+}
+
+hipError_t launch_fwd_poly(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                           int H_kv, int N_q, int N_k, int d, bool causal, float scale, int poly_quarters,
+                           hipStream_t stream) {
+    switch (poly_quarters) {
+        case 1: return launch_fwd_poly_t<1>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal, scale, stream);
+        case 2: return launch_fwd_poly_t<2>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal, scale, stream);
+        case 4: return launch_fwd_poly_t<4>(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal, scale, stream);
+        default: return launch_fwd(Q, K, V, O, LSE, B, H, H_kv, N_q, N_k, d, causal, scale, stream);
+    }
+}
+
+namespace {
+__global__ __launch_bounds__(256) void exp2_poly_kernel(const float* __restrict__ x, float* __restrict__ y,
+                                                        long long n) {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+        y[i] = exp2_poly(x[i]);
+}
+}  // namespace
+
+hipError_t launch_exp2_poly(const float* x, float* y, long long n, hipStream_t stream) {
+    const long long blocks = std::min<long long>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(exp2_poly_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n);
+    return hipGetLastError();
 }
 
 }  // namespace fa

@@ -31,6 +31,14 @@ constexpr int kDecHeadsPerBlock = 16;
 hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
                       int H_kv, int N_q, int N_k, int d, bool causal, float scale, hipStream_t stream);
 
+// The forward with poly_quarters (1, 2 or 4) of every four softmax exponentials taken by the
+// FMA-unit polynomial exp2_poly instead of v_exp_f32 (any other value: launch_fwd).
+hipError_t launch_fwd_poly(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                           int H_kv, int N_q, int N_k, int d, bool causal, float scale, int poly_quarters,
+                           hipStream_t stream);
+// y[i] = exp2_poly(x[i]) for i < n (the forward's polynomial, for its error tests).
+hipError_t launch_exp2_poly(const float* x, float* y, long long n, hipStream_t stream);
+
 // Backward: D = rowsum(dO * O) into `workspace` (B*H*N_q floats), then dQ, then dK and dV.
 hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                       void* dQ, void* dK, void* dV, float* workspace, int B, int H, int H_kv, int N_q, int N_k, int d,

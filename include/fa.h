@@ -5,6 +5,8 @@
  *   fa_fwd           FlashAttention-2 forward: O = softmax(scale * Q K^T) V and the
  *                    per-row log-sum-exp, computed tile by tile with the online
  *                    softmax state (m, l, acc); S and P never reach device memory.
+ *   fa_fwd_poly_exp2 the forward with part of the softmax exponentials taken by a
+ *                    polynomial on the FMA units (FA4's exp2 trick).
  *   fa_bwd           FlashAttention backward: dQ, dK, dV from dO, recomputing P on
  *                    chip from the saved log-sum-exp.
  *   fa_decode_split  flash-decoding, step 2: one query token per sequence, keys cut
@@ -82,6 +84,31 @@ typedef enum {
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
            int N_q, int N_k, int d, int causal, float scale, void* stream);
+
+/*
+ * The forward of fa_fwd with a software exponential for part of the softmax (the
+ * FA4 softmax trick of computing some exponentials with a polynomial on the FMA units
+ * instead of the transcendental unit; CUDA Kernel interview course, FlashAttention v4
+ * card).  Of every four exponentials a lane takes, the first poly_quarters (1, 2 or 4)
+ * use p(x) = 2^n * (1 + f (c1 + c2 f + c3 f^2)), x = n + f, n = floor(x), with a
+ * minimax cubic of relative error <= 8.6e-5 (exact at integer x); the rest use
+ * v_exp_f32.  Each probability then carries a relative error <= 8.6e-5, so LSE moves by
+ * at most about 8.6e-5 and O by at most about 2 * 8.6e-5 * max|V| from fa_fwd's result.
+ * Arguments, layouts and limits as for fa_fwd; poly_quarters outside {1, 2, 4} gives
+ * FA_ERR_ARG.  On gfx950 the transcendental instruction costs less than the
+ * polynomial's eight FMA-unit instructions, so this path is slower than fa_fwd; it is
+ * offered for the error analysis and for hardware where the balance differs.
+ */
+int fa_fwd_poly_exp2(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int H_kv,
+                     int N_q, int N_k, int d, int causal, float scale, int poly_quarters, void* stream);
+
+/*
+ * The polynomial exponential of fa_fwd_poly_exp2 on its own: y[i] = 2^x[i] for
+ * 0 <= i < n, as the forward computes it (relative error <= 8.6e-5 for x >= -126;
+ * x <= -200 and -inf give 0).  x and y are device arrays of n floats, 4-byte aligned;
+ * n = 0 enqueues nothing.  For tests of the error bound.
+ */
+int fa_exp2_poly(const float* x, float* y, long long n, void* stream);
 
 /*
  * Exact attention backward (Lecture 11 section 5.1): for the forward above with the

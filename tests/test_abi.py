@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fp8_quantize", "fa_fwd_fp8", "fa_fp8_block_rows",
                  "fa_decode_split", "fa_decode_split_paged", "fa_combine", "fa_decode_num_splits",
-                 "fa_decode_workspace_bytes", "fa_strerror", "fa_fwd_tile_shape", "fa_fwd_tile_count"):
+                 "fa_decode_workspace_bytes", "fa_strerror", "fa_fwd_tile_shape", "fa_fwd_tile_count",
+                 "fa_fwd_poly_exp2", "fa_exp2_poly"):
         assert want in names
 
 
@@ -60,6 +61,29 @@ P_MIS = ctypes.c_void_p(0x100004)   # 4-byte aligned only
 
 def fwd(lib, Q=P, K=P, V=P, O=P, L=P, B=1, H=1, H_kv=1, N_q=8, N_k=8, d=64, causal=0, scale=0.125):
     return lib.fa_fwd(Q, K, V, O, L, B, H, H_kv, N_q, N_k, d, causal, scale, None)
+
+
+def fwd_poly(lib, Q=P, K=P, V=P, O=P, L=P, B=1, H=1, H_kv=1, N_q=8, N_k=8, d=64, causal=0, scale=0.125, quarters=1):
+    return lib.fa_fwd_poly_exp2(Q, K, V, O, L, B, H, H_kv, N_q, N_k, d, causal, scale, quarters, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL), (dict(L=None), fa.FA_ERR_NULL), (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(H=3, H_kv=2), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED), (dict(O=P_MIS), fa.FA_ERR_ALIGN),
+    (dict(scale=0.0), fa.FA_ERR_ARG), (dict(causal=2), fa.FA_ERR_ARG),
+    (dict(quarters=0), fa.FA_ERR_ARG), (dict(quarters=3), fa.FA_ERR_ARG), (dict(quarters=5), fa.FA_ERR_ARG),
+    (dict(quarters=-1), fa.FA_ERR_ARG),
+])
+def test_fwd_poly_exp2_validation(lib, kw, status):
+    assert fwd_poly(lib, **kw) == status
+
+
+def test_exp2_poly_validation(lib):
+    assert lib.fa_exp2_poly(None, P, 4, None) == fa.FA_ERR_NULL
+    assert lib.fa_exp2_poly(P, None, 4, None) == fa.FA_ERR_NULL
+    assert lib.fa_exp2_poly(P, P, -1, None) == fa.FA_ERR_SHAPE
+    assert lib.fa_exp2_poly(ctypes.c_void_p(0x100002), P, 4, None) == fa.FA_ERR_ALIGN
+    assert lib.fa_exp2_poly(P, P, 0, None) == fa.FA_OK  # nothing to do: no launch
 
 
 def bwd(lib, Q=P, K=P, V=P, O=P, dO=P, L=P, dQ=P, dK=P, dV=P, W=P, B=1, H=2, H_kv=1, N_q=8, N_k=8, d=64, causal=0,
