@@ -476,9 +476,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(const uint16_t* __
     }
 }
 
-// One wave per (b, h): lse = M + ln sum_s e^(lse_s - M); O = sum_s e^(lse_s - lse) o_s.
-// Lane t holds segment t's weight (t < 64 per pass); the o_s rows are then read with all
-// loads of a pass in flight and the weights broadcast from their lanes.
+// One wave per (b, h): lse = M + ln l and O = acc / l, with M = max_s lse_s,
+// l = sum_s e^(lse_s - M) and acc = sum_s e^(lse_s - M) o_s, taken online over chunks of CH
+// segments: a chunk's LSE values and partial rows are all requested before any is used (one
+// memory round trip per chunk, the kernel's whole cost at small S), then the running M, l
+// and acc are rescaled if the chunk raises M.  Lane l holds columns DPL*l .. DPL*l + DPL-1.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ O_part,
                                                       const float* __restrict__ LSE_part,
@@ -486,47 +488,59 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int BH, int S) {
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr int DPL = D / 64;  // outputs per lane
+    constexpr int CH = 16;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= BH) return;
     const float* lp = LSE_part + (int64_t)row * S;
-    float M = -INFINITY;
-    for (int t = lane; t < S; t += 64) M = fmaxf(M, lp[t]);
-    for (int k = 32; k >= 1; k >>= 1) M = xor_max(M, k);
-    float o[DPL];
+    const float* op = O_part + (int64_t)row * S * D + lane * DPL;
+    float M = -INFINITY, l = 0.f, acc[DPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] = 0.f;
-    float lse = -INFINITY;
-    if (M != -INFINITY) {
-        float sum = 0.f;
-        for (int t = lane; t < S; t += 64) sum += exp2_hw((lp[t] - M) * kLog2e);
-        for (int k = 32; k >= 1; k >>= 1) sum = xor_sum(sum, k);
-        lse = M + log2_hw(sum) * kLn2;
-        const float* op = O_part + (int64_t)row * S * D + lane * DPL;
-        for (int t0 = 0; t0 < S; t0 += 64) {
-            const int t = t0 + lane;
-            const float wl = t < S ? exp2_hw((lp[t] - lse) * kLog2e) : 0.f;  // 0 for empty segments
-            const int n = min(64, S - t0);
-            int u = 0;
-            for (; u + 8 <= n; u += 8) {
-                float x[8][DPL];
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    for (int t0 = 0; t0 < S; t0 += CH) {
+        float ls[CH], x[CH][DPL];
 #pragma unroll
-                for (int a = 0; a < 8; ++a)
-#pragma unroll
-                    for (int k = 0; k < DPL; ++k) x[a][k] = op[(int64_t)(t0 + u + a) * D + k];
-#pragma unroll
-                for (int a = 0; a < 8; ++a) {
-                    const float wgt = __shfl(wl, u + a, 64);
-#pragma unroll
-                    for (int k = 0; k < DPL; ++k) o[k] = fmaf(wgt, x[a][k], o[k]);
-                }
-            }
-            for (; u < n; ++u) {
-                const float wgt = __shfl(wl, u, 64);
-#pragma unroll
-                for (int k = 0; k < DPL; ++k) o[k] = fmaf(wgt, op[(int64_t)(t0 + u) * D + k], o[k]);
+        for (int j = 0; j < CH; ++j) {
+            const int t = min(t0 + j, S - 1);  // past the end: a repeat, weighted 0 below
+            ls[j] = lp[t];
+            if constexpr (DPL == 2) {
+                const float2 v = *reinterpret_cast<const float2*>(op + (int64_t)t * D);
+                x[j][0] = v.x;
+                x[j][1] = v.y;
+            } else {
+                x[j][0] = op[(int64_t)t * D];
             }
         }
+        float Mc = M;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (t0 + j >= S) ls[j] = -INFINITY;
+            Mc = fmaxf(Mc, ls[j]);
+        }
+        if (Mc == -INFINITY) continue;  // only empty segments so far
+        const float r = exp2_hw((M - Mc) * kLog2e);  // 0 while M = -inf
+        l *= r;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] *= r;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const float w = exp2_hw((ls[j] - Mc) * kLog2e);  // 0 for empty segments
+            l += w;
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, x[j][k], acc[k]);
+        }
+        M = Mc;
+    }
+    float o[DPL];
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) o[k] = acc[k] * inv;
+        lse = M + log2_hw(l) * kLn2;
+    } else {
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) o[k] = 0.f;
     }
     uint16_t* dst = O + (int64_t)row * D + lane * DPL;
     if constexpr (DPL == 2) {
