@@ -62,6 +62,8 @@ FUSED = [
     (1, 2, 1, 100, 128, 60),     # trailing segments empty
     (2, 20, 1, 515, 128, 5),     # 20 query heads per K/V head: two head groups, two counters
     (3, 6, 3, 37, 128, 2),
+    (1, 64, 1, 300, 128, 3),     # 64 query heads per K/V head: four head chunks, four counters
+    (2, 128, 2, 257, 64, 4),
 ]
 
 

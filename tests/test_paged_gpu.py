@@ -116,6 +116,7 @@ PAGED = [
     (2, 8, 2, (300, 5000), 128, 256, 3),
     (1, 16, 1, (64,), 64, 16, 3),             # trailing segments empty
     (2, 4, 1, (33, 47), 128, 16, 1),
+    (2, 128, 2, (300, 129), 64, 32, 3),       # 64 query heads per K/V head: four head chunks
     (1, 4, 1, (20000,), 128, 16, 1),         # one segment of 625 blocks: a wave's blocks past its
                                              # 128th read the block table directly
 ]

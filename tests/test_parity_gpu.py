@@ -234,6 +234,8 @@ DECODE = [
     (2, 20, 1, 515, 128, 5),     # 20 query heads per K/V head: two head chunks
     (1, 16, 1, 64, 64, 3),
     (3, 6, 3, 37, 128, 2),
+    (1, 64, 1, 300, 128, 3),     # the largest group (64 query heads per K/V head): four head chunks
+    (2, 128, 2, 257, 64, 4),
 ]
 
 
