@@ -181,7 +181,7 @@ def bwd_flops(B, H, N_q, N_k, d, causal):
 
 
 def leg_backward(fa, torch, reps, B=16, H=16, H_kv=16, N=1024, seed=2):
-    """fa_bwd (D pre-pass, dQ kernel, dK/dV kernel) on the batched-prefill shape, O and LSE
+    """fa_bwd (dQ kernel with D = rowsum(dO * O), then the dK/dV kernel) on the batched-prefill shape, O and LSE
     from fa_fwd on the same inputs; d = 64 with and without the causal mask, d = 128 without."""
     import gen
 

@@ -3,7 +3,7 @@
 // What is computed (Lecture 11 section 5.1): the gradients of sum(dO * O) with respect to
 // Q, K and V, given dO and the forward's O and LSE.  P is recomputed on chip from the
 // saved log-sum-exp (P = exp(S - LSE), one exp per score) instead of being stored:
-//   D_i = dO_i . O_i                  (Exercise 6's identity; bwd_dot_kernel)
+//   D_i = dO_i . O_i                  (Exercise 6's identity; bwd_dq_kernel, per row)
 //   dV  = P^T dO,   dP = dO V^T,   dS = P * (dP - D)
 //   dK  = scale * dS^T Q              (bwd_dkdv_kernel: one workgroup per 128 keys)
 //   dQ  = scale * dS K                (bwd_dq_kernel: one workgroup per 128 query rows)
@@ -118,38 +118,17 @@ __device__ __forceinline__ void take_row_frags(const u32x4 (&raw)[D / 16], bool 
     }
 }
 
-// ---------------------------------------------------------------------------- D = rowsum(dO * O)
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ Dv, int64_t rows) {
-    constexpr int CPR = D / 8;  // lanes per row, 16 bytes each
-    constexpr int RPB = 256 / CPR;
-    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
-    const int c = threadIdx.x % CPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + 8 * c);
-        const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + 8 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = fmaf(bf16_bits_to_f32(a[e] & 0xffffu), bf16_bits_to_f32(g[e] & 0xffffu), acc);
-            acc = fmaf(bf16_bits_to_f32(a[e] >> 16), bf16_bits_to_f32(g[e] >> 16), acc);
-        }
-    }
-#pragma unroll
-    for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
-    if (row < rows && c == 0) Dv[row] = acc;
-}
-
 // ---------------------------------------------------------------------------- dQ
 // One workgroup of 4 waves per (b, h, 128 query rows); wave w owns 32 rows, lane = row.
+// Its prologue also forms D_i = dO_i . O_i of its rows and writes it for the dK/dV kernel.
 // Per key tile: S^T = K Q^T and dP^T = V dO^T (A = K, V rows), P^T = 2^(c S^T - L2),
 // dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (A = K^T through transposing reads of the same
 // K tile).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                                        const float* __restrict__ LSE, const float* __restrict__ Dv,
+                                                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
+                                                        const uint16_t* __restrict__ dO,
+                                                        const float* __restrict__ LSE, float* __restrict__ Dv,
                                                         uint16_t* __restrict__ dQ, int H, int H_kv, int N_q, int N_k,
                                                         int T_r, int BH, float c, float scale) {
     constexpr int BR = kBwdBlockRows, BC = bwd_dq_block_cols(D), TILE = BC * D;
@@ -193,15 +172,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
     // All loads are issued (rows clamped to N_q - 1) before any value is taken.
     const int q_ld = min(q_row, N_q - 1);
     const float lse_raw = LSE[(int64_t)bh * N_q + q_ld];
-    const float dd_raw = Dv[(int64_t)bh * N_q + q_ld];
-    u32x4 q_raw[D / 16], do_raw[D / 16];
+    u32x4 q_raw[D / 16], do_raw[D / 16], o_raw[D / 16];
     issue_row_loads<D>(Q + q_base + (int64_t)q_ld * D, hh, q_raw);
     issue_row_loads<D>(dO + q_base + (int64_t)q_ld * D, hh, do_raw);
+    issue_row_loads<D>(O + q_base + (int64_t)q_ld * D, hh, o_raw);
     bf16x8 qf[D / 16], dof[D / 16];
     take_row_frags<D>(q_raw, q_row < N_q, qf);
     take_row_frags<D>(do_raw, q_row < N_q, dof);
     const float l2 = q_row < N_q ? (lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e) : INFINITY;
-    const float dd = q_row < N_q ? dd_raw : 0.f;
+    // D = dO . O of this row (Exercise 6's identity): each half of the wave holds half of the
+    // row's elements of dO (dof) and of O; the halves are added.  Written for the dK/dV kernel.
+    float dd = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 a = vgpr_copy(o_raw[ks]);
+        const u32x4 gv = __builtin_bit_cast(u32x4, dof[ks]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dd = fmaf(bf16_bits_to_f32(a[e] & 0xffffu), bf16_bits_to_f32(gv[e] & 0xffffu), dd);
+            dd = fmaf(bf16_bits_to_f32(a[e] >> 16), bf16_bits_to_f32(gv[e] >> 16), dd);
+        }
+    }
+    dd = half_swap_sum(dd);  // rows past N_q: dof is zero, so dd = 0
+    if (hh == 0 && q_row < N_q) Dv[(int64_t)bh * N_q + q_row] = dd;
     const Offsets<D> o = operand_offsets<D>(lane);
 
     f32x16 acc[D / 32];
@@ -674,19 +667,14 @@ hipError_t launch_bwd_t(const void* Q, const void* K, const void* V, const void*
                         void* dQ, void* dK, void* dV, float* Dv, int B, int H, int H_kv, int N_q, int N_k,
                         float scale, hipStream_t stream) {
     const float c = (float)((double)scale * 1.4426950408889634073599);
-    const int64_t rows = (int64_t)B * H * N_q;
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(O), static_cast<const uint16_t*>(dO), Dv, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int T_r = (N_q + kBwdBlockRows - 1) / kBwdBlockRows;
     const int n_qr = CAUSAL ? (T_r + 1) / 2 : T_r;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)n_qr * B * H)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-                       static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(dO), LSE, Dv,
+                       static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(O),
+                       static_cast<const uint16_t*>(dO), LSE, Dv,
                        static_cast<uint16_t*>(dQ), H, H_kv, N_q, N_k, T_r, B * H, c, scale);
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int T_k = (N_k + kBwdBlockKeys - 1) / kBwdBlockKeys;
     const int n_kr = CAUSAL ? (T_k + 1) / 2 : T_k;

@@ -39,7 +39,8 @@ hipError_t launch_fwd_poly(const void* Q, const void* K, const void* V, void* O,
 // y[i] = exp2_poly(x[i]) for i < n (the forward's polynomial, for its error tests).
 hipError_t launch_exp2_poly(const float* x, float* y, long long n, hipStream_t stream);
 
-// Backward: D = rowsum(dO * O) into `workspace` (B*H*N_q floats), then dQ, then dK and dV.
+// Backward: dQ (its kernel also writes D = rowsum(dO * O) into `workspace`, B*H*N_q floats),
+// then dK and dV.
 hipError_t launch_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
                       void* dQ, void* dK, void* dV, float* workspace, int B, int H, int H_kv, int N_q, int N_k, int d,
                       bool causal, float scale, hipStream_t stream);

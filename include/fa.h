@@ -129,7 +129,8 @@ int fa_exp2_poly(const float* x, float* y, long long n, void* stream);
  *   workspace  fa_bwd_workspace_bytes(B, H, N_q) bytes of device memory, 16-byte
  *              aligned, owned by the caller; it receives D (fp32) and may be reused
  *              once the call's work on `stream` has finished.
- * Limits: as for fa_fwd.  The three kernels run in order on `stream`.
+ * Limits: as for fa_fwd.  The two kernels (dQ, which also writes D, then dK/dV) run
+ * in order on `stream`.
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
            void* dQ, void* dK, void* dV, float* workspace, int B, int H, int H_kv, int N_q, int N_k, int d,
