@@ -173,10 +173,12 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restri
     if (kind != 2) return;  // uniform per workgroup
     __syncthreads();
     // Transposed, key-permuted tile: D rows (channels) x 64 positions; 16 bytes per thread.
+    // The lanes of a wave take consecutive channels of one 16-position group, so every LDS
+    // read instruction reads one key row (64 consecutive bytes, no bank conflicts).
     uint8_t* tile = Vt8 + ((int64_t)head * TK + t) * (D * kFp8KRows);
 #pragma unroll
     for (int q = tid; q < D * 4; q += 256) {
-        const int j = q >> 2, p0 = 16 * (q & 3);
+        const int j = q % D, p0 = 16 * (q / D);
         uint32_t wv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
