@@ -40,6 +40,24 @@ __device__ __forceinline__ int vt_key(int p) {
     return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * h + (e & 3);
 }
 
+// Value of lane (lane xor M), M in {1, 2, 4, 8}, by DPP lane moves inside 16-lane rows (no LDS
+// traffic, unlike a general shuffle): xor 1 and 2 are quad permutations [1,0,3,2] and
+// [2,3,0,1]; xor 4 mirrors each 8-lane half (lane 8r + i takes 8r + 7 - i) and then reverses
+// each quad, which together take lane 8r + 4a + b from 8r + 4(1 - a) + b; xor 8 rotates the
+// 16-lane row by 8.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8, "DPP lane exchange inside a 16-lane row");
+    const int x = __float_as_int(v);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+    if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+    if constexpr (M == 4) {
+        const int y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        return __int_as_float(__builtin_amdgcn_mov_dpp(y, 0x1B, 0xF, 0xF, false));  // quad [3,2,1,0]
+    }
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror:8
+}
+
 // ---------------------------------------------------------------------------- quantisation
 // One workgroup of 256 threads per block of rows (a query block of kFp8QRows rows or a
 // key/value tile of kFp8KRows keys).  D/8 consecutive lanes hold one row, 8 elements each
@@ -132,7 +150,9 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restri
                 const bool upper = (sub & ls) != 0;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float o = __shfl_xor(x[p][e], ls, kWave);
+                    const float v = x[p][e];
+                    const float o = ls == 1 ? lane_xor<1>(v) : ls == 2 ? lane_xor<2>(v) : ls == 4 ? lane_xor<4>(v)
+                                                                                          : lane_xor<8>(v);
                     x[p][e] = upper ? o - x[p][e] : x[p][e] + o;
                 }
             }
