@@ -147,13 +147,15 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restri
                     }
 #pragma unroll
             for (int ls = 1; ls < LPR; ls <<= 1) {  // stage len = 8 * ls
-                const bool upper = (sub & ls) != 0;
+                // upper lane: o - x, lower lane: x + o, as one fma with x's sign chosen per lane
+                // (x * -1 is exact, so the single rounding is that of the subtraction)
+                const float sgn = (sub & ls) != 0 ? -1.f : 1.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float v = x[p][e];
                     const float o = ls == 1 ? lane_xor<1>(v) : ls == 2 ? lane_xor<2>(v) : ls == 4 ? lane_xor<4>(v)
                                                                                           : lane_xor<8>(v);
-                    x[p][e] = upper ? o - x[p][e] : x[p][e] + o;
+                    x[p][e] = fmaf(v, sgn, o);
                 }
             }
         }
