@@ -39,6 +39,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -73,8 +74,12 @@ def kernel_source_hash(kernel: str) -> str:
         raise KeyError("no source list for kernel %r" % kernel)
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[family]:
-        with open(os.path.join(ROOT, "exact_attention_59_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_59_amd", "csrc", name)) as f:
+            text = f.read()
+        # comments and layout do not change a kernel: hash the code tokens only
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

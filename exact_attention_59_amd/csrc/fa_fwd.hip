@@ -19,7 +19,10 @@
 //     workgroup can see, and a wave skips tiles its own rows cannot see; only tiles
 //     crossing the diagonal or the ragged end of K are masked element-wise;
 //   - under the causal mask a workgroup takes two query tiles, i and T_r-1-i, so every
-//     workgroup does the same work (no tail of long tiles);
+//     workgroup does the same work (no tail of long tiles); the order of the two is chosen
+//     per head dimension for L2 reuse of K/V (end of the kernel);
+//   - optionally (POLY > 0) part of the exponentials are computed by a cubic on the FMA
+//     units instead of the transcendental instruction (the FA4 softmax trick);
 //   - workgroup ids are mapped so that the workgroups of a head share an XCD (and its
 //     L2) and are resident together.
 //
