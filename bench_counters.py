@@ -116,12 +116,15 @@ def sq_summary(run_dir: str, cmd: str) -> str:
     if not files:
         raise SystemExit("no counter_collection.csv under %s" % run_dir)
     per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    dur = defaultdict(dict)  # key -> {(file, dispatch): duration in ns}
     for f in files:
         for row in csv.DictReader(open(f)):
             m = re.search(SQ_KERNELS, row["Kernel_Name"])
             if m:
                 key = "%s grid=%s" % (short_name(m.group(1)), row["Grid_Size"])
                 per[key][row["Counter_Name"]][(f, row["Dispatch_Id"])] += float(row["Counter_Value"])
+                if "End_Timestamp" in row:
+                    dur[key][(f, row["Dispatch_Id"])] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
     import bench
 
     names = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_MFMA",
@@ -131,18 +134,25 @@ def sq_summary(run_dir: str, cmd: str) -> str:
              "GPU cycles = GRBM_GUI_ACTIVE / %d XCDs (the launch's duration in cycles); MFMA busy %% = "
              "SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles x %d SIMDs); VALU active %% = "
              "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES (the waves' share of cycles issuing VALU); conflicts / LDS instr = "
-             "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS." % (XCDS, SIMDS), "",
-             "| kernel | GPU cycles | MFMA busy % | VALU active % | MFMA instr | VALU instr | LDS instr | LDS bank conflicts | conflicts / LDS instr |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS; clock = GPU cycles / the dispatch's duration in the same run "
+             "(profiled launches run longer than plain ones); MFMA busy at 2.4 GHz = MFMA busy %% x clock / 2.4 GHz, "
+             "the share of the nominal-clock peak the matrix cores delivered." % (XCDS, SIMDS), "",
+             "| kernel | GPU cycles | clock GHz | MFMA busy % | MFMA busy at 2.4 GHz % | VALU active % | MFMA instr | VALU instr | LDS instr | LDS bank conflicts | conflicts / LDS instr |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     table = {}
     for key in sorted(per):
         avg = {n: (sum(per[key][n].values()) / len(per[key][n])) if per[key][n] else float("nan") for n in names}
         gpu = avg["GRBM_GUI_ACTIVE"] / XCDS
-        table[key] = {"source_hash": bench.kernel_source_hash(key), "gpu_cycles": round(gpu), "mfma_busy_pct": round(100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS), 2)
+        clocks = [per[key]["GRBM_GUI_ACTIVE"][d] / XCDS / ns for d, ns in dur[key].items()
+                  if ns > 0 and d in per[key]["GRBM_GUI_ACTIVE"]]
+        ghz = sum(clocks) / len(clocks) if clocks else float("nan")
+        busy = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS) if gpu else float("nan")
+        table[key] = {"source_hash": bench.kernel_source_hash(key), "gpu_cycles": round(gpu),
+                      "clock_ghz": round(ghz, 3) if clocks else None, "mfma_busy_pct": round(100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS), 2)
                       if gpu else None, "lds_instr": round(avg["SQ_INSTS_LDS"]),
                       "lds_bank_conflicts": round(avg["SQ_LDS_BANK_CONFLICT"])}
-        lines.append("| %s | %.0f | %.1f | %.1f | %.0f | %.0f | %.0f | %.0f | %.4f |" % (
-            key, gpu, 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * SIMDS) if gpu else float("nan"),
+        lines.append("| %s | %.0f | %.2f | %.1f | %.1f | %.1f | %.0f | %.0f | %.0f | %.0f | %.4f |" % (
+            key, gpu, ghz, busy, busy * ghz / 2.4,
             100.0 * avg["SQ_ACTIVE_INST_VALU"] / avg["SQ_WAVE_CYCLES"] if avg["SQ_WAVE_CYCLES"] else float("nan"),
             avg["SQ_INSTS_MFMA"], avg["SQ_INSTS_VALU"], avg["SQ_INSTS_LDS"], avg["SQ_LDS_BANK_CONFLICT"],
             avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_INSTS_LDS"] if avg["SQ_INSTS_LDS"] else float("nan")))
