@@ -6,12 +6,15 @@ tile sizes 32, 64 and 128 are favoured), query/key length mismatches under the c
 mask, several query heads per key/value head, both head dimensions, and segment counts
 up to one key per segment; they stay small enough for the oracle to finish in seconds.
 """
+import os
+
 import numpy as np
 import pytest
 
 import gen
 import oracle
-from parity_util import bf16_dev_to_f64, check, check_grads, decode_inputs, fwd_inputs, say, scale_for, to_dev
+from parity_util import (bf16_dev_to_f64, check, check_grads, decode_inputs, fwd_inputs, o_rounding_allowance, say,
+                         scale_for, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +30,11 @@ def _length(rng, hi):
     return int(rng.integers(1, hi + 1))
 
 
+SEED = int(os.environ.get("FA_SWEEP_SEED", "59"))  # another seed draws another set of shapes
+
+
 def _shapes():
-    rng = np.random.default_rng(59)
+    rng = np.random.default_rng(SEED)
     fwd, dec, bwd = [], [], []
     for _ in range(16):
         H_kv = int(rng.integers(1, 4))
@@ -112,7 +118,13 @@ def test_sweep_bwd(orc, B, H, H_kv, N_q, N_k, d, causal):
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
     torch.cuda.synchronize()
     dQ, dK, dV, _ = orc.attention_bwd(Q, K, V, dO, causal=causal, scale=scale)
-    check_grads(name, (bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)), (dQ, dK, dV))
+    # The backward takes D = dO . O from the stored bf16 O; in rows that see one or two keys
+    # its rounding is not small against the nearly cancelling gradient, so the gates are
+    # applied after subtracting that first-order effect (o_rounding_allowance).
+    O_ref, L_ref = orc.attention(Q, K, V, causal=causal, scale=scale)
+    O_b = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    allow = o_rounding_allowance(Q, K, dO, O_ref, O_b, L_ref, scale, causal)
+    check_grads(name, (bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)), (dQ, dK, dV), allow)
     if causal and N_q > N_k:  # rows that see no key get exactly zero
         assert np.all(bf16_dev_to_f64(dq)[:, :, :N_q - N_k] == 0.0), name
 
