@@ -1,5 +1,5 @@
-"""GPU parity on seeded random shapes: forward, flash-decoding (two launches and one) and
-backward against the fp64 oracle, element by element.
+"""GPU parity on seeded random shapes: forward, flash-decoding (two launches and one, over a
+contiguous and over a paged cache) and backward against the fp64 oracle, element by element.
 
 The shapes are drawn once from a fixed seed and mix ragged lengths (values next to the
 tile sizes 32, 64 and 128 are favoured), query/key length mismatches under the causal
@@ -147,3 +147,44 @@ def test_sweep_decode_one_launch(orc, shared_counters, B, H, H_kv, N_k, d, S):
     O_ref, L_ref = orc.attention(Q, K, V)
     check(name, bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
     assert int(shared_counters.abs().sum()) == 0, name + ": a group counter was left non-zero"
+
+
+def _paged_shapes():
+    rng = np.random.default_rng(SEED + 1000)
+    out = []
+    for _ in range(8):
+        H_kv = int(rng.integers(1, 4))
+        group = int(rng.choice([1, 2, 4, 7, 16, 20]))
+        B = int(rng.integers(1, 4))
+        lens = tuple(int(rng.integers(0, 1500)) if rng.random() < 0.8 else _length(rng, 1500) for _ in range(B))
+        P = int(rng.choice([16, 32, 64, 128, 256]))
+        S = int(rng.integers(1, 40))
+        out.append((B, H_kv * group, H_kv, lens, int(rng.choice([64, 128])), P, S))
+    return out
+
+
+PAGED = _paged_shapes()
+
+
+@pytest.mark.parametrize("B,H,H_kv,lens,d,P,S", PAGED)
+def test_sweep_paged(orc, B, H, H_kv, lens, d, P, S):
+    """Paged flash-decoding (split + combine, and the one-launch form) over a shuffled pool
+    whose unowned pages hold NaN, on random lengths (empty sequences included), page sizes
+    and segment counts."""
+    from test_paged_gpu import make_paged, reference
+
+    name = "sweep paged%s" % str((B, H, H_kv, lens, d, P, S))
+    say(name)
+    N = max(1, max(lens))
+    Q, K, V = decode_inputs(5900 + N + P + S, B, H, H_kv, N, d)
+    Kp, Vp, table = make_paged(K, V, lens, P, seed=N + S + P)
+    q, kp, vp = to_dev(Q[:, :, 0, :]), to_dev(Kp), to_dev(Vp)
+    t = torch.from_numpy(table).cuda()
+    ln = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    o_part, l_part = fa.decode_split_paged(q, kp, vp, t, ln, S)
+    o, l = fa.combine(o_part, l_part)
+    o1, l1 = fa.decode_paged(q, kp, vp, t, ln, S)
+    torch.cuda.synchronize()
+    O_ref, L_ref = reference(orc, Q, K, V, lens)
+    check(name, bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
+    check(name + " one launch", bf16_dev_to_f64(o1), O_ref, l1.cpu().numpy(), L_ref)
