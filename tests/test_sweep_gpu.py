@@ -1,5 +1,6 @@
 """GPU parity on seeded random shapes: forward, flash-decoding (two launches and one, over a
-contiguous and over a paged cache) and backward against the fp64 oracle, element by element.
+contiguous and over a paged cache), backward and the FP8 path against the fp64 oracle, element
+by element.
 
 The shapes are drawn once from a fixed seed and mix ragged lengths (values next to the
 tile sizes 32, 64 and 128 are favoured), query/key length mismatches under the causal
@@ -188,3 +189,41 @@ def test_sweep_paged(orc, B, H, H_kv, lens, d, P, S):
     O_ref, L_ref = reference(orc, Q, K, V, lens)
     check(name, bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
     check(name + " one launch", bf16_dev_to_f64(o1), O_ref, l1.cpu().numpy(), L_ref)
+
+
+def _fp8_shapes():
+    rng = np.random.default_rng(SEED + 2000)
+    out = []
+    for _ in range(6):
+        H_kv = int(rng.integers(1, 3))
+        group = int(rng.choice([1, 2, 4]))
+        out.append((int(rng.integers(1, 3)), H_kv * group, H_kv, _length(rng, 600), _length(rng, 600),
+                    int(rng.choice([64, 128])), bool(rng.integers(0, 2))))
+    return out
+
+
+FP8 = _fp8_shapes()
+
+
+@pytest.mark.parametrize("B,H,H_kv,N_q,N_k,d,causal", FP8)
+def test_sweep_fp8(orc, B, H, H_kv, N_q, N_k, d, causal):
+    """The FP8 path on random shapes: quantiser codes and scales bit for bit against the
+    oracle's quantiser, the forward against the oracle on the dequantised and on the original
+    tensors (the FP8 gates)."""
+    from fp8_util import sign_mask
+    from parity_util import check_fp8
+    from test_fp8_gpu import quantize_both, run_fp8
+
+    name = "sweep fp8%s" % str((B, H, H_kv, N_q, N_k, d, causal))
+    say(name)
+    Q, K, V = fwd_inputs(5800 + N_q + 2 * N_k + d, B, H, H_kv, N_q, N_k, d)
+    lo, hi = sign_mask(N_q + 5 * N_k)
+    (q8, qs, k8, ks, v8, vs, pad), (oq, ok, ov), _ = quantize_both(orc, Q, K, V, lo, hi, True)
+    assert np.array_equal(q8, oq[0]) and np.array_equal(qs.view(np.uint32), oq[1].view(np.uint32)), name + " Q"
+    assert np.array_equal(k8, ok[0]) and np.array_equal(ks.view(np.uint32), ok[1].view(np.uint32)), name + " K"
+    assert np.array_equal(v8, ov[0]) and np.array_equal(vs.view(np.uint32), ov[1].view(np.uint32)), name + " V"
+    o, l, (qd, kd, vd) = run_fp8(orc, Q, K, V, causal, lo, hi)
+    sc = scale_for(d)
+    O_q, L_q = orc.attention(qd, kd, vd, causal=causal, scale=sc)
+    O_x, L_x = orc.attention(Q, K, V, causal=causal, scale=sc)
+    check_fp8(name, o, O_q, l, L_q, O_x, L_x)
