@@ -306,3 +306,25 @@ def test_combine_synthetic_partials(orc, S, d):
             L_ref[b, h], O_ref[b, h] = orc.lse_combine(lse_s[b, h].astype(np.float64), o_s[b, h].astype(np.float64))
     check("combine synthetic S=%d d=%d" % (S, d), bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
     assert np.all(bf16_dev_to_f64(o)[1, 2] == 0.0)
+
+
+@pytest.mark.parametrize("scale", [1e-3, 0.05, 1.0, 4.0])
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_fwd_and_decode_scale_range(orc, scale, d, causal):
+    """Softmax scales from nearly uniform (1e-3) to sharply peaked (4.0: scores span hundreds of
+    units, the running max moves on most tiles) in the forward and in flash-decoding."""
+    B, H, H_kv, N = 1, 4, 2, 333
+    name = "scale %g d=%d causal=%s" % (scale, d, causal)
+    say(name)
+    Q, K, V = fwd_inputs(4400 + d, B, H, H_kv, N, N, d)
+    o, l = run_fwd(Q, K, V, causal, scale=scale)
+    O_ref, L_ref = orc.attention(Q, K, V, causal=causal, scale=scale)
+    check("fwd " + name, bf16_dev_to_f64(o), O_ref, l.cpu().numpy(), L_ref)
+    q = to_dev(Q[:, :, :1, :])
+    o_part, l_part = fa.decode_split(q[:, :, 0, :], to_dev(K), to_dev(V), 5, scale=scale)
+    od, ld = fa.combine(o_part, l_part)
+    o1, l1 = fa.decode(q[:, :, 0, :], to_dev(K), to_dev(V), 5, scale=scale)
+    torch.cuda.synchronize()
+    O_d, L_d = orc.attention(Q[:, :, :1], K, V, scale=scale)
+    check("decode " + name, bf16_dev_to_f64(od), O_d[:, :, 0], ld.cpu().numpy(), L_d[:, :, 0])
+    check("one-launch decode " + name, bf16_dev_to_f64(o1), O_d[:, :, 0], l1.cpu().numpy(), L_d[:, :, 0])
