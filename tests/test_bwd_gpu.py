@@ -144,3 +144,24 @@ def test_bwd_gqa_ragged_sampled(orc):
         qs, ks = (slice(b, b + 1), slice(g * G, g * G + G)), (slice(b, b + 1), slice(g, g + 1))
         dQ, dK, dV, _ = orc.attention_bwd(Q[qs], K[ks], V[ks], dO[qs], causal=True, scale=scale)
         check_grads("%s group b=%d g=%d" % (name, b, g), (dq[qs], dk[ks], dv[ks]), (dQ, dK, dV))
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.5])
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_bwd_scale_range(orc, scale, d, causal):
+    """Gradients at a nearly flat (0.02) and a peaked (0.5: scores of a row span tens of units)
+    softmax scale, fed the oracle's O (as bf16) and LSE, with the O-rounding allowance."""
+    B, H, H_kv, N_q, N_k = 1, 4, 2, 200, 333
+    name = "bwd scale %g d=%d causal=%s" % (scale, d, causal)
+    say(name)
+    Q, K, V = fwd_inputs(950 + d, B, H, H_kv, N_q, N_k, d)
+    dO = gen.normal_bf16(950 + d, gen.TENSOR_DO, (B, H, N_q, d))
+    O_ref, L_ref = orc.attention(Q, K, V, causal=causal, scale=scale)
+    O_b = gen.f32_to_bf16(O_ref.astype(np.float32))
+    q, k, v, do, o = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO), to_dev(O_b)
+    lse = torch.from_numpy(L_ref.astype(np.float32)).to("cuda:0")
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    dQ, dK, dV, _ = orc.attention_bwd(Q, K, V, dO, causal=causal, scale=scale)
+    allow = o_rounding_allowance(Q, K, dO, O_ref, O_b, L_ref, scale, causal)
+    check_grads(name, (bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)), (dQ, dK, dV), allow)

@@ -63,6 +63,7 @@ CASES = [
     (2, 2, 1, 200, 333, 128, False),
     (2, 4, 4, 300, 300, 64, True),
     (1, 2, 2, 257, 700, 64, False),
+    (1, 2, 2, 333, 200, 64, True),   # N_q > N_k: leading rows see no key (O = 0, LSE = -inf)
 ]
 
 
@@ -113,3 +114,17 @@ def test_fwd_poly_exp2_long_causal(orc, quarters):
     l1, l0 = lse.double(), lse0.double()
     allow = -np.log1p(-(BOUND + EVAL)) + 4 * 2.0 ** -23 * torch.clamp(l0.abs(), min=1.0)
     assert bool(((l1 - l0).abs() <= allow).all()), name
+
+
+@pytest.mark.parametrize("quarters", [1, 2, 4])
+def test_fwd_poly_exp2_one_key_is_exact(quarters):
+    """N_k = 1: the only score is the row maximum, whose exponent is exactly 0, and the
+    polynomial gives 2^0 = 1 exactly, so O is the V row bit for bit, as with fa_fwd."""
+    from parity_util import fwd_inputs as inputs
+
+    Q, K, V = inputs(9300 + quarters, 2, 4, 2, 37, 1, 128)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    o, _ = fa.fwd(q, k, v, poly_exp2=quarters)
+    torch.cuda.synchronize()
+    g = torch.arange(4, device="cuda") // 2
+    assert torch.equal(o, v[:, g, :1].expand_as(o))
