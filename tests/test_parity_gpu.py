@@ -328,3 +328,35 @@ def test_fwd_and_decode_scale_range(orc, scale, d, causal):
     O_d, L_d = orc.attention(Q[:, :, :1], K, V, scale=scale)
     check("decode " + name, bf16_dev_to_f64(od), O_d[:, :, 0], ld.cpu().numpy(), L_d[:, :, 0])
     check("one-launch decode " + name, bf16_dev_to_f64(o1), O_d[:, :, 0], l1.cpu().numpy(), L_d[:, :, 0])
+
+
+def test_fwd_long_sequence_sampled(orc):
+    """N_q = N_k = 32768 causal (256 query tiles per head, 512 key tiles): sampled rows against
+    the oracle, including the last rows, which see every key."""
+    B, H, H_kv, N, d = 1, 2, 1, 32768, 128
+    name = "fwd long sequence N=%d" % N
+    say(name)
+    Q, K, V = fwd_inputs(4500, B, H, H_kv, N, N, d)
+    o, lse = run_fwd(Q, K, V, True)
+    rows = np.unique(np.concatenate([sample_rows(B, H, N, 48, 4500), [N - 1, 2 * N - 1, N // 2]]))
+    O_ref, L_ref = orc.attention(Q, K, V, causal=True, rows=rows)
+    check(name + " (%d sampled rows)" % rows.size, bf16_dev_to_f64(o).reshape(-1, d)[rows], O_ref,
+          lse.cpu().numpy().astype(np.float64).reshape(-1)[rows], L_ref)
+
+
+def test_decode_million_key_cache(orc):
+    """One sequence with 2^20 cached keys (512 MB of K and V): the split + combine and the
+    one-launch decode against the oracle."""
+    B, H, H_kv, N_k, d = 1, 8, 1, 1 << 20, 128
+    name = "decode N_k=2^20"
+    say(name)
+    Q, K, V = decode_inputs(4600, B, H, H_kv, N_k, d)
+    q, k, v = to_dev(Q[:, :, 0, :]), to_dev(K), to_dev(V)
+    S = fa.decode_num_splits(B, H_kv, N_k, d)
+    o_part, l_part = fa.decode_split(q, k, v, S)
+    o, l = fa.combine(o_part, l_part)
+    o1, l1 = fa.decode(q, k, v, S)
+    torch.cuda.synchronize()
+    O_ref, L_ref = orc.attention(Q, K, V)
+    check(name + " S=%d" % S, bf16_dev_to_f64(o), O_ref[:, :, 0], l.cpu().numpy(), L_ref[:, :, 0])
+    check(name + " one launch", bf16_dev_to_f64(o1), O_ref[:, :, 0], l1.cpu().numpy(), L_ref[:, :, 0])
