@@ -162,26 +162,26 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     const int dma_r0 = w * C::DMA_PER_WAVE * ROWS_PER_COPY + lane / (D / 8);
     const int dma_sc = lane % (D / 8);
     const uint32_t dma_lds_off = __builtin_amdgcn_readfirstlane(w * C::DMA_PER_WAVE * 1024);  // bytes
-    // At d = 64 a whole tile is copied from a wave-uniform base with fixed per-lane byte
-    // offsets (K and V swizzles), which keeps the address arithmetic off the vector ALUs;
-    // the ragged last tile (and d = 128, whose registers are full) clamps rows per lane.
-    uint32_t dma_voff[2][C::DMA_PER_WAVE];
-    if constexpr (D == 64) {
+    // A whole tile is copied from a wave-uniform base address (scalar registers, advanced by
+    // 1 KB per copy) plus fixed per-lane byte offsets, which keeps the address arithmetic off
+    // the vector ALUs.  V's swizzle repeats within every copy's rows, so one offset serves
+    // all of V's copies; K's differs per copy.  The ragged last tile clamps rows per lane.
+    uint32_t dma_koff[C::DMA_PER_WAVE];
 #pragma unroll
-        for (int t = 0; t < C::DMA_PER_WAVE; ++t) {
-            const int r = dma_r0 + t * ROWS_PER_COPY;
-            dma_voff[0][t] = 2u * (uint32_t)(r * D + 8 * (dma_sc ^ swz_k<D>(r)));
-            dma_voff[1][t] = 2u * (uint32_t)(r * D + 8 * (dma_sc ^ swz_v<D>(r)));
-        }
+    for (int t = 0; t < C::DMA_PER_WAVE; ++t) {
+        const int r = dma_r0 + t * ROWS_PER_COPY;
+        dma_koff[t] = 2u * (uint32_t)(dma_r0 * D + 8 * (dma_sc ^ swz_k<D>(r)));
     }
+    const uint32_t dma_voff = 2u * (uint32_t)(dma_r0 * D + 8 * (dma_sc ^ swz_v<D>(dma_r0)));
     auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* dst, bool is_v) {
         const int key0 = j * BC;
         const uint16_t* head = src + kv_base;
-        if (D == 64 && key0 + BC <= N_k) {
+        if (key0 + BC <= N_k) {
             const uint16_t* tile = head + (int64_t)key0 * D;
 #pragma unroll
             for (int t = 0; t < C::DMA_PER_WAVE; ++t)
-                copy_to_lds16_sbase(tile, dma_voff[is_v][t], lds_addr(dst) + dma_lds_off + t * 1024);
+                copy_to_lds16_sbase(tile + t * 512, is_v ? dma_voff : dma_koff[t],
+                                    lds_addr(dst) + dma_lds_off + t * 1024);
             return;
         }
 #pragma unroll
