@@ -68,7 +68,7 @@ FA_EXPORT const char* fa_strerror(int status) {
 
 FA_EXPORT int fa_fwd_tile_shape(int d, int* block_rows, int* block_cols) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if (block_rows) *block_rows = fa::kFwdBlockRows;
+    if (block_rows) *block_rows = fa::fwd_block_rows(d);
     if (block_cols) *block_cols = fa::fwd_block_cols(d);
     return FA_OK;
 }
@@ -77,7 +77,7 @@ FA_EXPORT int fa_fwd_tile_shape(int d, int* block_rows, int* block_cols) {
 // n_i stops at the last key visible to the tile's last real row.
 FA_EXPORT long long fa_fwd_tile_count(int N_q, int N_k, int d, int causal) {
     if (N_q <= 0 || N_k <= 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1)) return -1;
-    const long long BR = fa::kFwdBlockRows, BC = fa::fwd_block_cols(d);
+    const long long BR = fa::fwd_block_rows(d), BC = fa::fwd_block_cols(d);
     const long long T_r = (N_q + BR - 1) / BR, T_c = (N_k + BC - 1) / BC;
     if (!causal) return T_r * T_c;
     long long total = 0;
@@ -98,7 +98,7 @@ static int check_fwd(const void* Q, const void* K, const void* V, const void* O,
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H * N_q * d >= kMaxElems || (long long)B * H_kv * N_k * d >= kMaxElems)
         return FA_ERR_UNSUPPORTED;
-    const long long blocks = (long long)((N_q + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * H;
+    const long long blocks = (long long)((N_q + fa::fwd_block_rows(d) - 1) / fa::fwd_block_rows(d)) * B * H;
     if (blocks > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(LSE)) return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;

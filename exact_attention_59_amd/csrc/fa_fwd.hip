@@ -24,7 +24,8 @@
 //   - optionally (POLY > 0) part of the exponentials are computed by a cubic on the FMA
 //     units instead of the transcendental instruction (the FA4 softmax trick);
 //   - workgroup ids are mapped so that the workgroups of a head share an XCD (and its
-//     L2) and are resident together.
+//     L2) and are resident together;
+//   - the output tile is staged through LDS so that every store writes whole rows.
 //
 // Register layout: the scores are computed transposed, S^T = K_j Q_i^T, with
 // v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = head dim).  A lane then holds
@@ -49,13 +50,15 @@ namespace {
 
 template <int D>
 struct FwdCfg {
-    static constexpr int BR = kFwdBlockRows;  // query rows per workgroup
+    static constexpr int NW = fwd_waves(D);       // waves per workgroup
+    static constexpr int BR = fwd_block_rows(D);  // query rows per workgroup (32 per wave)
     static constexpr int BC = fwd_block_cols(D);  // keys per tile
-    static constexpr int THREADS = 256;
+    static constexpr int THREADS = 64 * NW;
     static constexpr int TILE = BC * D;       // elements of one K or V tile buffer (rows unpadded)
-    // A 64-lane global->LDS copy moves 1 KB; the 4 waves split a tile's copies evenly.
-    static constexpr int DMA_PER_WAVE = BC * D * 2 / 1024 / 4;
-    static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * 4 * 1024 == BC * D * 2, "tile must split into 1 KB copies");
+    // A 64-lane global->LDS copy moves 1 KB; the waves split a tile's copies evenly.
+    static constexpr int DMA_PER_WAVE = BC * D * 2 / 1024 / NW;
+    static_assert(BR == 32 * NW, "each wave owns 32 query rows");
+    static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * NW * 1024 == BC * D * 2, "tile must split into 1 KB copies");
 };
 
 // LDS tiles are row-major without padding; the 16-byte chunks of row r are stored at
@@ -78,12 +81,12 @@ constexpr float kRescaleSlack = 8.0f;
 // wave per SIMD covers latency that two leave exposed; two at d = 128 (its MFMA tiles and
 // accumulators need up to 256 VGPRs).
 template <int D>
-constexpr int kFwdBlocksPerCU = D == 64 ? 3 : 2;
+constexpr int kFwdBlocksPerCU = D == 64 ? 3 : 8 / fwd_waves(D);
 
 // POLY (0..4): of every four exponentials of a lane's softmax, the first POLY are taken with
 // exp2_poly on the FMA units and the rest with v_exp_f32 (0 = all on the transcendental unit).
 template <int D, bool CAUSAL, int POLY = 0>
-__global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(FwdCfg<D>::THREADS, kFwdBlocksPerCU<D>) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -104,7 +107,8 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
     asm volatile("" ::"s"(O), "s"(LSE));
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int l32 = lane & 31, hh = lane >> 5;
 
     // Causal rows get longer with the query index, so a causal workgroup takes the pair of
@@ -390,21 +394,38 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
         if (j + 1 < n_tiles) step(std::integral_constant<bool, true>{}, j + 1, sB, sA);
     }
 
-    // Epilogue: O = acc / l (once), LSE = (m + log2 l) ln 2.
+    // Epilogue: O = acc / l (once), LSE = (m + log2 l) ln 2.  A lane holds 4-element pieces of
+    // its query row; the wave stages its 32 rows in its own slice of the K buffers (idle: every
+    // read of the loop completed before its last barrier, and no copy is in flight), with the
+    // same chunk swizzle as K, and reads them back as whole rows, so that each store writes
+    // complete rows instead of 8-byte pieces of 32 rows.
     lsum = half_swap_sum(lsum);
-    if (q_row < N_q) {
+    {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        uint16_t* op = O + q_base + (int64_t)q_row * D;
+        static_assert(C::NW == 4 && C::TILE >= 64 * D, "two waves' rows per K buffer");
+        uint16_t* const stage = (w < 2 ? k_lds0 : k_lds1) + (w & 1) * 32 * D;
+        // A fresh lane index, so that no lane-derived value from before the loop stays live
+        // across it to be reused here.
+        int el;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(el));
+        const int er = el & 31, eh = el >> 5, sw = swz_k<D>(er);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int d0 = 32 * db + 8 * gq + 4 * hh;
-                *reinterpret_cast<u32x2*>(op + d0) =
+            for (int gq = 0; gq < 4; ++gq)
+                *reinterpret_cast<u32x2*>(stage + er * D + 8 * ((4 * db + gq) ^ sw) + 4 * eh) =
                     u32x2{pack_bf16x2(acc[db][4 * gq + 0] * inv, acc[db][4 * gq + 1] * inv),
                           pack_bf16x2(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv)};
-            }
-        if (hh == 0) LSE[(int64_t)bh * N_q + q_row] = lsum > 0.f ? (m2 + log2_hw(lsum)) * kLn2 : -INFINITY;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes land before its reads
+        constexpr int ROWS = 512 / D;  // rows per 64-lane read of 16 bytes a lane
+#pragma unroll
+        for (int i = 0; i < 32 / ROWS; ++i) {
+            const int r = ROWS * i + el / (D / 8), ch = el % (D / 8);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * D + 8 * (ch ^ swz_k<D>(r)));
+            if (q0w + r < N_q) *reinterpret_cast<u32x4*>(O + q_base + (int64_t)(q0w + r) * D + 8 * ch) = v;
+        }
+        if (hh == 0 && q_row < N_q)
+            LSE[(int64_t)bh * N_q + q_row] = lsum > 0.f ? (m2 + log2_hw(lsum)) * kLn2 : -INFINITY;
     }
   };
 
@@ -426,11 +447,12 @@ __global__ __launch_bounds__(256, kFwdBlocksPerCU<D>) void fwd_kernel(const uint
 template <int D, bool CAUSAL, int POLY = 0>
 hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
                         int H_kv, int N_q, int N_k, float scale, hipStream_t stream) {
-    const int T_r = (N_q + kFwdBlockRows - 1) / kFwdBlockRows;
+    constexpr int BR = FwdCfg<D>::BR;
+    const int T_r = (N_q + BR - 1) / BR;
     const int BH = B * H;
     const float c = (float)((double)scale * 1.4426950408889634073599);
     const long long blocks = (long long)(CAUSAL ? (T_r + 1) / 2 : T_r) * BH;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLY>), dim3((unsigned)blocks), dim3(FwdCfg<D>::THREADS), 0, stream,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                        static_cast<const uint16_t*>(V), static_cast<uint16_t*>(O), LSE, H, H_kv, N_q, N_k,
                        T_r, BH, c);

@@ -7,9 +7,10 @@
 
 namespace fa {
 
-// Forward tile shape: query rows per workgroup, and keys per tile for head dimension d
-// (the same for both head dimensions).
-constexpr int kFwdBlockRows = 128;
+// Forward tile shape for head dimension d: waves per workgroup (each owns 32 query rows),
+// query rows per workgroup, and keys per tile.
+constexpr int fwd_waves(int /*d*/) { return 4; }
+constexpr int fwd_block_rows(int d) { return 32 * fwd_waves(d); }
 constexpr int fwd_block_cols(int /*d*/) { return 64; }
 
 // Backward tile shapes: the dQ kernel's query rows per workgroup and keys per tile; the
