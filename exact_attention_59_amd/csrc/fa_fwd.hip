@@ -397,8 +397,9 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, kFwdBlocksPerCU<D>) void fwd_ke
     // Epilogue: O = acc / l (once), LSE = (m + log2 l) ln 2.  A lane holds 4-element pieces of
     // its query row; the wave stages its 32 rows in its own slice of the K buffers (idle: every
     // read of the loop completed before its last barrier, and no copy is in flight), with the
-    // same chunk swizzle as K, and reads them back as whole rows, so that each store writes
-    // complete rows instead of 8-byte pieces of 32 rows.
+    // same chunk swizzle as K and the two 8-byte halves of a chunk exchanged in rows 16..31 (so
+    // that the 32 rows of one write hit 32 distinct bank pairs), and reads them back as whole
+    // rows, so that each store writes complete rows instead of 8-byte pieces of 32 rows.
     lsum = half_swap_sum(lsum);
     {
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, kFwdBlocksPerCU<D>) void fwd_ke
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq)
-                *reinterpret_cast<u32x2*>(stage + er * D + 8 * ((4 * db + gq) ^ sw) + 4 * eh) =
+                *reinterpret_cast<u32x2*>(stage + er * D + 8 * ((4 * db + gq) ^ sw) + 4 * (eh ^ (er >> 4))) =
                     u32x2{pack_bf16x2(acc[db][4 * gq + 0] * inv, acc[db][4 * gq + 1] * inv),
                           pack_bf16x2(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv)};
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes land before its reads
@@ -421,7 +422,8 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, kFwdBlocksPerCU<D>) void fwd_ke
 #pragma unroll
         for (int i = 0; i < 32 / ROWS; ++i) {
             const int r = ROWS * i + el / (D / 8), ch = el % (D / 8);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * D + 8 * (ch ^ swz_k<D>(r)));
+            u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * D + 8 * (ch ^ swz_k<D>(r)));
+            if (r >= 16) v = u32x4{v[2], v[3], v[0], v[1]};
             if (q0w + r < N_q) *reinterpret_cast<u32x4*>(O + q_base + (int64_t)(q0w + r) * D + 8 * ch) = v;
         }
         if (hh == 0 && q_row < N_q)
