@@ -258,19 +258,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
         __syncthreads();
     }
 
-    // dQ = scale * acc; register r of acc[db] holds d = 32*db + 8*(r/4) + 4*hh + r%4.
-    if (q_row < N_q) {
-        uint16_t* op = dQ + q_base + (int64_t)q_row * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int d0 = 32 * db + 8 * gq + 4 * hh;
-                *reinterpret_cast<u32x2*>(op + d0) =
-                    u32x2{pack_bf16x2(acc[db][4 * gq + 0] * scale, acc[db][4 * gq + 1] * scale),
-                          pack_bf16x2(acc[db][4 * gq + 2] * scale, acc[db][4 * gq + 3] * scale)};
-            }
-    }
+    // dQ = scale * acc (register r of acc[db] holds d = 32*db + 8*(r/4) + 4*hh + r%4), staged
+    // in the wave's own tile buffer (idle: every read of the loop completed before its last
+    // barrier, and no copy is in flight) and stored as whole rows.
+    static_assert(TILE >= 32 * D, "a tile buffer holds a wave's 32 rows");
+    store_rows_staged<D>(acc, scale, w == 0 ? k_s0 : w == 1 ? k_s1 : w == 2 ? v_s0 : v_s1,
+                         dQ + q_base + (int64_t)q0w * D, N_q - q0w);
   };
 
     run(CAUSAL ? T_r - 1 - rank : rank);

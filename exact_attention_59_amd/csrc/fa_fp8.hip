@@ -426,21 +426,16 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
             if (j + 1 < n_tiles) step(std::integral_constant<bool, true>{}, j + 1);
         }
 
+        // Epilogue: the wave stages its rows in one of the four tile buffers (idle: every read of
+        // the loop completed before its last barrier, and no copy is in flight) and stores them
+        // as whole rows.
         lsum = half_swap_sum(lsum);
-        if (q_row < N_q) {
-            const float f = lsum > 0.f ? sv_max / lsum : 0.f;
-            uint16_t* op = O + ((int64_t)bh * N_q + q_row) * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int d0 = 32 * db + 8 * gq + 4 * hh;
-                    *reinterpret_cast<u32x2*>(op + d0) =
-                        u32x2{pack_bf16x2(acc[db][4 * gq + 0] * f, acc[db][4 * gq + 1] * f),
-                              pack_bf16x2(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
-                }
-            if (hh == 0) LSE[(int64_t)bh * N_q + q_row] = lsum > 0.f ? (m2 + log2_hw(lsum)) * kLn2 : -INFINITY;
-        }
+        static_assert(TILE >= 32 * D * 2, "a tile buffer holds a wave's 32 output rows");
+        uint8_t* const stage = w == 0 ? k_lds0 : w == 1 ? k_lds1 : w == 2 ? v_lds0 : v_lds1;
+        store_rows_staged<D>(acc, lsum > 0.f ? sv_max / lsum : 0.f, reinterpret_cast<uint16_t*>(stage),
+                             O + ((int64_t)bh * N_q + q0w) * D, N_q - q0w);
+        if (hh == 0 && q_row < N_q)
+            LSE[(int64_t)bh * N_q + q_row] = lsum > 0.f ? (m2 + log2_hw(lsum)) * kLn2 : -INFINITY;
     };
 
     run_tile(CAUSAL ? T_r - 1 - rank : rank);

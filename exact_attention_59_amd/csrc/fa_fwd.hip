@@ -394,44 +394,15 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, kFwdBlocksPerCU<D>) void fwd_ke
         if (j + 1 < n_tiles) step(std::integral_constant<bool, true>{}, j + 1, sB, sA);
     }
 
-    // Epilogue: O = acc / l (once), LSE = (m + log2 l) ln 2.  A lane holds 4-element pieces of
-    // its query row; the wave stages its 32 rows in its own slice of the K buffers (idle: every
-    // read of the loop completed before its last barrier, and no copy is in flight), and reads
-    // them back as whole rows, so that each store writes complete rows instead of 8-byte pieces
-    // of 32 rows.  Staged layout: the 16-byte chunk k of row r sits at chunk k ^ (r % chunks per
-    // row), its two 8-byte halves exchanged when bit 3 of r is set.  An 8-byte LDS write is
-    // served 16 lanes at a time over 32 four-byte banks (measured on gfx950 with the bank
-    // conflict counter), and the 16 rows of such a group then fill 16 distinct 8-byte slots.
+    // Epilogue: O = acc / l (once), LSE = (m + log2 l) ln 2.  The wave stages its rows in its
+    // own slice of the K buffers, which are idle: every read of the loop completed before its
+    // last barrier, and no copy is in flight.
     lsum = half_swap_sum(lsum);
-    {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        static_assert(C::NW == 4 && C::TILE >= 64 * D, "two waves' rows per K buffer");
-        uint16_t* const stage = (w < 2 ? k_lds0 : k_lds1) + (w & 1) * 32 * D;
-        // A fresh lane index, so that no lane-derived value from before the loop stays live
-        // across it to be reused here.
-        int el;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(el));
-        constexpr int CH = D / 8;  // 16-byte chunks per row
-        const int er = el & 31, eh = el >> 5, sw = er & (CH - 1);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-                *reinterpret_cast<u32x2*>(stage + er * D + 8 * ((4 * db + gq) ^ sw) + 4 * (eh ^ ((er >> 3) & 1))) =
-                    u32x2{pack_bf16x2(acc[db][4 * gq + 0] * inv, acc[db][4 * gq + 1] * inv),
-                          pack_bf16x2(acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv)};
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes land before its reads
-        constexpr int ROWS = 512 / D;  // rows per 64-lane read of 16 bytes a lane
-#pragma unroll
-        for (int i = 0; i < 32 / ROWS; ++i) {
-            const int r = ROWS * i + el / CH, ch = el % CH;
-            u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * D + 8 * (ch ^ (r & (CH - 1))));
-            if ((ROWS * i) & 8) v = u32x4{v[2], v[3], v[0], v[1]};  // bit 3 of r (ROWS >= 4)
-            if (q0w + r < N_q) *reinterpret_cast<u32x4*>(O + q_base + (int64_t)(q0w + r) * D + 8 * ch) = v;
-        }
-        if (hh == 0 && q_row < N_q)
-            LSE[(int64_t)bh * N_q + q_row] = lsum > 0.f ? (m2 + log2_hw(lsum)) * kLn2 : -INFINITY;
-    }
+    static_assert(C::NW == 4 && C::TILE >= 64 * D, "two waves' rows per K buffer");
+    store_rows_staged<D>(acc, lsum > 0.f ? 1.f / lsum : 0.f, (w < 2 ? k_lds0 : k_lds1) + (w & 1) * 32 * D,
+                         O + q_base + (int64_t)q0w * D, N_q - q0w);
+    if (hh == 0 && q_row < N_q)
+        LSE[(int64_t)bh * N_q + q_row] = lsum > 0.f ? (m2 + log2_hw(lsum)) * kLn2 : -INFINITY;
   };
 
     // Order of a causal pair.  At d = 64 the long tile goes first: the workgroups of a head
