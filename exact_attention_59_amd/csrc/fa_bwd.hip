@@ -429,21 +429,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         __syncthreads();
     }
 
-    // dK = scale * accK, dV = accV; register r of lane holds key k0w + 8*(r/4) + 4*hh + r%4
-    // at d = 32*db + l32.
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int k = k0w + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (k < N_k) {
-            uint16_t* kp = dK + kv_base + (int64_t)k * D + l32;
-            uint16_t* vp = dV + kv_base + (int64_t)k * D + l32;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                kp[32 * db] = (uint16_t)(pack_bf16x2(accK[db][r] * scale, 0.f) & 0xffffu);
-                vp[32 * db] = (uint16_t)(pack_bf16x2(accV[db][r], 0.f) & 0xffffu);
-            }
-        }
-    }
+    // dK = scale * accK, dV = accV (register r of lane holds key k0w + 8*(r/4) + 4*hh + r%4 at
+    // d = 32*db + l32), staged in the wave's own Q/dO buffer (idle: every read of the loop
+    // completed before its last barrier, and no copy is in flight) and stored as whole rows.
+    static_assert(QT >= 2 * 32 * D, "a Q/dO buffer holds a wave's dK and dV rows");
+    uint16_t* const slice = w == 0 ? q_s0 : w == 1 ? q_s1 : w == 2 ? o_s0 : o_s1;
+    store_cols_staged<D>(accK, scale, slice, dK + kv_base + (int64_t)k0w * D, N_k - k0w);
+    store_cols_staged<D>(accV, 1.f, slice + 32 * D, dV + kv_base + (int64_t)k0w * D, N_k - k0w);
   };
 
     run(kr);
@@ -634,18 +626,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         __syncthreads();
     }
 
-    // register r of lane holds key k0w + 8*(r/4) + 4*hh + r%4 at d = 32*db + l32
-    uint16_t* out = ds_wave ? dK : dV;
-    const float f = ds_wave ? scale : 1.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int k = k0w + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (k < N_k) {
-            uint16_t* op = out + kv_base + (int64_t)k * D + l32;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) op[32 * db] = (uint16_t)(pack_bf16x2(acc[db][r] * f, 0.f) & 0xffffu);
-        }
-    }
+    // register r of lane holds key k0w + 8*(r/4) + 4*hh + r%4 at d = 32*db + l32; staged in
+    // half of a Q/dO buffer (idle: every read of the loop completed before its last barrier, and
+    // no copy is in flight) and stored as whole rows.
+    static_assert(QT >= 2 * 32 * D, "a Q/dO buffer holds two waves' rows");
+    uint16_t* const slice = (w < 4 ? (w < 2 ? q_s0 : q_s1) : (w < 6 ? o_s0 : o_s1)) + (w & 1) * 32 * D;
+    store_cols_staged<D>(acc, ds_wave ? scale : 1.f, slice, (ds_wave ? dK : dV) + kv_base + (int64_t)k0w * D,
+                         N_k - k0w);
   };
 
     run(kr);

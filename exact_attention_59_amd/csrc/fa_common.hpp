@@ -222,6 +222,41 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], f
     }
 }
 
+// Output epilogue of the kernels that keep one output column per lane: acc[db][r] holds row
+// 8*(r/4) + 4*hh + r%4 of the wave's 32 rows at column d = 32*db + l32.  The values are scaled
+// by f, rounded to bf16 (RNE), written to `stage` (32 * D elements of LDS that no other wave
+// touches before the caller's next barrier) two bytes a lane, and stored as whole rows, 16
+// bytes a lane: row r goes to out + r * D when r < rows.  Staged layout: the 16-byte chunk k of
+// row r sits at chunk k ^ (4 * (r / 4) mod chunks per row), so that the two half-waves' rows
+// of one write (r and r + 4) fall on different banks; the whole-row reads see every chunk of
+// a row once.
+template <int D>
+__device__ __forceinline__ void store_cols_staged(const f32x16 (&acc)[D / 32], float f, uint16_t* stage,
+                                                  uint16_t* __restrict__ out, int rows) {
+    constexpr int CH = D / 8;      // 16-byte chunks per row
+    constexpr int ROWS = 512 / D;  // rows per 64-lane read of 16 bytes a lane
+    int el;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(el));
+    const int l32 = el & 31, hh = el >> 5;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier LDS reads of the slice are done
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int sw = 4 * ((row >> 2) & (CH / 4 - 1));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            stage[row * D + 8 * ((4 * db + (l32 >> 3)) ^ sw) + (l32 & 7)] =
+                (uint16_t)(pack_bf16x2(acc[db][r] * f, 0.f) & 0xffffu);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes land before its reads
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+        const int r = ROWS * i + el / CH, ch = el % CH;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * D + 8 * (ch ^ (4 * ((r >> 2) & (CH / 4 - 1)))));
+        if (r < rows) *reinterpret_cast<u32x4*>(out + (int64_t)r * D + 8 * ch) = v;
+    }
+}
+
 // s_waitcnt vmcnt(0): this wave's global->LDS copies have landed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
