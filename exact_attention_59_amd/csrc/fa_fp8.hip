@@ -265,9 +265,28 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     for (int i = lane; i < T_c; i += 64) sv_max = fmaxf(sv_max, vsh[i]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) sv_max = fmaxf(sv_max, __shfl_xor(sv_max, m, kWave));
+    const float inv_sv_max = sv_max > 0.f ? 1.f / sv_max : 0.f;
 
-    // Copy helpers: copy u of this wave fills 1 KB block (w * CPW + u) of a tile.
+    // Copy helpers: copy u of this wave fills 1 KB block (w * CPW + u) of a tile.  A whole tile
+    // is copied from a wave-uniform base (scalar registers, advanced by 1 KB per copy) plus fixed
+    // per-lane byte offsets; the ragged last K tile clamps rows per lane.  V^T tiles are padded
+    // to whole tiles by the quantiser, and their swizzle repeats within every copy's rows, so
+    // one offset serves all of V's copies.
+    uint32_t koff[CPW];
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+        const int row = (w * CPW + u) * (1024 / D) + lane / KCH;
+        koff[u] = (uint32_t)((lane / KCH) * D + 16 * ((lane % KCH) ^ swz_k8<D>(row)));
+    }
+    const uint32_t voff = (uint32_t)((lane / 4) * BC + 16 * ((lane % 4) ^ swz_v8(w * CPW * 16 + lane / 4)));
     auto dma_k = [&](int j, uint8_t* dst) {
+        if ((j + 1) * BC <= N_k) {
+            const uint8_t* tile = kh + (int64_t)j * BC * D;
+#pragma unroll
+            for (int u = 0; u < CPW; ++u)
+                copy_to_lds16_sbase(tile + (w * CPW + u) * 1024, koff[u], lds_addr(dst + (w * CPW + u) * 1024));
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < CPW; ++u) {
             const int blk = w * CPW + u;
@@ -278,14 +297,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
         }
     };
     auto dma_v = [&](int j, uint8_t* dst) {
+        const uint8_t* tile = vh + (int64_t)j * TILE;
 #pragma unroll
-        for (int u = 0; u < CPW; ++u) {
-            const int blk = w * CPW + u;
-            const int row = blk * 16 + lane / 4;
-            const int ch = (lane % 4) ^ swz_v8(row);
-            const uint8_t* gp = vh + (int64_t)j * TILE + row * BC + 16 * ch;
-            copy_to_lds16(gp, lds_addr(dst + blk * 1024));
-        }
+        for (int u = 0; u < CPW; ++u)
+            copy_to_lds16_sbase(tile + (w * CPW + u) * 1024, voff, lds_addr(dst + (w * CPW + u) * 1024));
     };
     // A-operand reads: 32 bytes of row `row` at logical chunks c0, c0 + 1.
     auto read32 = [&](const uint8_t* base, int row, int rowbytes, int c0, int sw) -> i32x8 {
@@ -361,8 +376,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
                 const float sk = ksh[j], sv = vsh[j];
                 // score factor (kept positive, so that a masked -inf stays -inf)
                 const float cs = fmaxf(c * sq * sk, 1.17549435e-38f);
-                const float lv = sv > 0.f ? log2_hw(sv / sv_max) : 0.f;
-                const float wv = sv > 0.f ? sv_max / sv : 1.f;
+                // per-tile weights from reciprocals (v_rcp_f32, about 1 ulp) instead of divisions
+                const float lv = sv > 0.f ? log2_hw(sv * inv_sv_max) : 0.f;
+                const float wv = sv > 0.f ? sv_max * __builtin_amdgcn_rcpf(sv) : 1.f;
                 const int key0 = j * BC;
                 if (key0 + BC > N_k || (CAUSAL && key0 + BC - 1 > q0w + off)) {
                     const int lim = (CAUSAL ? min(N_k - 1, q_row + off) : N_k - 1) - key0 - 4 * hh;
