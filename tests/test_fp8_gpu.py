@@ -137,8 +137,8 @@ def test_fp8_incoherent_processing_lowers_error(orc):
     assert errs[True][0] < 0.6 * errs[False][0] and errs[True][1] < 0.6 * errs[False][1]
 
 
-@pytest.mark.parametrize("B,H,H_kv,N,d,causal", [(16, 16, 16, 1024, 64, False), (2, 16, 16, 8192, 128, True),
-                                                (4, 32, 8, 4095, 128, True)])
+@pytest.mark.parametrize("B,H,H_kv,N,d,causal", [(16, 16, 16, 1024, 64, False), (16, 16, 16, 1024, 64, True),
+                                                (2, 16, 16, 8192, 128, True), (4, 32, 8, 4095, 128, True)])
 def test_fp8_fwd_workload_sampled(orc, B, H, H_kv, N, d, causal):
     """Full workload shapes (batched prefill, long causal, grouped heads with a ragged length)
     on sampled rows."""

@@ -166,6 +166,7 @@ FULL = [
     ("single-head N=256 d=64 (fp32 draw)", 1, 1, 1, 1, 256, 64, False, 0),
     ("batched prefill 16x16 N=1024 d=64", 2, 16, 16, 16, 1024, 64, False, 1024),
     ("batched prefill 16x16 N=1024 d=64 causal", 2, 16, 16, 16, 1024, 64, True, 1024),
+    ("batched prefill 16x16 N=1024 d=128", 2, 16, 16, 16, 1024, 128, False, 1024),
     ("long causal 2x16 N=8192 d=128", 3, 2, 16, 16, 8192, 128, True, 512),
     ("GQA ragged 4x32/8 N=4095 d=128 causal", 4, 4, 32, 8, 4095, 128, True, 512),
 ]
