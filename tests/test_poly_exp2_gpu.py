@@ -91,23 +91,31 @@ def test_fwd_poly_exp2_parity(orc, quarters, B, H, H_kv, N_q, N_k, d, causal):
     assert dl.max() > 0.0, "%s: no exponential went through the polynomial" % name
 
 
-@pytest.mark.parametrize("quarters", [1, 4])
-def test_fwd_poly_exp2_long_causal(orc, quarters):
-    """The long causal workload (B=2 H=16 N=8192 d=128) with polynomial exponentials, launched as
-    the benchmark launches it: sampled rows against the oracle, every row's LSE within the
-    derived bound of fa_fwd's."""
+WORKLOADS = [
+    # name, seed, B, H, N, d, causal
+    ("batched prefill N=1024 d=64", 2, 16, 16, 1024, 64, False),
+    ("long causal N=8192 d=128", 3, 2, 16, 8192, 128, True),
+]
+
+
+@pytest.mark.parametrize("quarters", [1, 2, 4])
+@pytest.mark.parametrize("name,seed,B,H,N,d,causal", WORKLOADS, ids=[w[0] for w in WORKLOADS])
+def test_fwd_poly_exp2_workloads(orc, quarters, name, seed, B, H, N, d, causal):
+    """The workloads the benchmark times with polynomial exponentials, launched as it launches
+    them: sampled rows against the oracle, every row's LSE within the derived bound of
+    fa_fwd's."""
     from parity_util import sample_rows
 
-    B, H, H_kv, N, d = 2, 16, 16, 8192, 128
-    name = "fwd poly exp2 q=%d long causal" % quarters
+    H_kv = H
+    name = "fwd poly exp2 q=%d %s" % (quarters, name)
     say(name)
-    Q, K, V = fwd_inputs(3, B, H, H_kv, N, N, d)
+    Q, K, V = fwd_inputs(seed, B, H, H_kv, N, N, d)
     q, k, v = to_dev(Q), to_dev(K), to_dev(V)
-    o, lse = fa.fwd(q, k, v, causal=True, poly_exp2=quarters)
-    o0, lse0 = fa.fwd(q, k, v, causal=True)
+    o, lse = fa.fwd(q, k, v, causal=causal, poly_exp2=quarters)
+    o0, lse0 = fa.fwd(q, k, v, causal=causal)
     torch.cuda.synchronize()
-    rows = sample_rows(B, H, N, 256, 3)
-    O_ref, L_ref = orc.attention(Q, K, V, causal=True, rows=rows)
+    rows = sample_rows(B, H, N, 256, seed)
+    O_ref, L_ref = orc.attention(Q, K, V, causal=causal, rows=rows)
     O_gpu = bf16_dev_to_f64(o).reshape(-1, d)[rows]
     L_gpu = lse.cpu().numpy().astype(np.float64).reshape(-1)[rows]
     check(name + " (%d sampled rows)" % rows.size, O_gpu, O_ref, L_gpu, L_ref)
